@@ -1,0 +1,258 @@
+// abi.cpp -- the extern "C" entry points declared in include/c3.h. Each one takes the library
+// mutex, validates its arguments before any launch, and converts C++ exceptions into a status.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <exception>
+#include <limits>
+
+#include "c3_internal.h"
+
+namespace c3 {
+const char* last_error_text();
+c3_status init_device(int hip_device);
+void finalize_device();
+c3_status stream_for_role(int role, const uint32_t* mask, hipStream_t* out);
+c3_status user_stream_create(const uint32_t* mask, int n_words, hipStream_t* out);
+c3_status user_stream_destroy(hipStream_t s);
+c3_status ensure_flush_buffer(size_t bytes);
+c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_conc_opts* o,
+                         c3_timing* t);
+
+c3_status copy_segments(const c3_copy_args& a, std::vector<Segment>* segs, size_t* dst_bytes) {
+    segs->clear();
+    if (!a.dst) return fail(C3_E_INVALID, "copy: dst is NULL");
+    if (a.kind == C3_COPY_GATHER) {
+        if (a.n_shards < 0 || a.n_shards > C3_MAX_SEGMENTS)
+            return fail(C3_E_INVALID, "gather: n_shards must be in [0, %d]", C3_MAX_SEGMENTS);
+        if (a.n_shards > 0 && !a.shards) return fail(C3_E_INVALID, "gather: shards array is NULL");
+        if (a.shard_bytes && (uint64_t)a.n_shards > std::numeric_limits<uint64_t>::max() / a.shard_bytes)
+            return fail(C3_E_INVALID, "gather: size overflow");
+        const size_t total = (size_t)a.n_shards * a.shard_bytes;
+        *dst_bytes = total;
+        if (total == 0) return C3_OK;
+        C3_TRY(check_device_ptr(a.dst, total, "gather dst"));
+        for (int i = 0; i < a.n_shards; ++i) {
+            C3_TRY(check_device_ptr(a.shards[i], a.shard_bytes, "gather shard"));
+            if (ranges_overlap(a.shards[i], a.shard_bytes, a.dst, total))
+                return fail(C3_E_OVERLAP, "gather: shard %d overlaps dst", i);
+            segs->push_back({a.shards[i], static_cast<char*>(a.dst) + (size_t)i * a.shard_bytes,
+                             a.shard_bytes});
+        }
+        return C3_OK;
+    }
+    if (a.kind == C3_COPY_ALL2ALL) {
+        if (a.grid < 1 || (int64_t)a.grid * a.grid > C3_MAX_SEGMENTS)
+            return fail(C3_E_INVALID, "all2all: grid must be in [1, 64]");
+        if (!a.src) return fail(C3_E_INVALID, "all2all: src is NULL");
+        const uint64_t nb = (uint64_t)a.grid * (uint64_t)a.grid;
+        if (a.block_bytes && nb > std::numeric_limits<uint64_t>::max() / a.block_bytes)
+            return fail(C3_E_INVALID, "all2all: size overflow");
+        const size_t total = (size_t)(nb * a.block_bytes);
+        *dst_bytes = total;
+        if (total == 0) return C3_OK;
+        C3_TRY(check_device_ptr(a.src, total, "all2all src"));
+        C3_TRY(check_device_ptr(a.dst, total, "all2all dst"));
+        if (ranges_overlap(a.src, total, a.dst, total))
+            return fail(C3_E_OVERLAP, "all2all: src overlaps dst");
+        for (int i = 0; i < a.grid; ++i)
+            for (int j = 0; j < a.grid; ++j) {
+                const size_t from = ((size_t)i * a.grid + j) * a.block_bytes;
+                const size_t to = ((size_t)j * a.grid + i) * a.block_bytes;
+                segs->push_back({static_cast<const char*>(a.src) + from,
+                                 static_cast<char*>(a.dst) + to, a.block_bytes});
+            }
+        return C3_OK;
+    }
+    return fail(C3_E_INVALID, "copy: unknown kind %d", a.kind);
+}
+
+// Isolated copy on `stream`: CU mover enqueues; SDMA mover drains the stream, issues, waits.
+c3_status copy_isolated(const c3_copy_args& a, hipStream_t stream) {
+    std::vector<Segment> segs;
+    size_t dst_bytes = 0;
+    C3_TRY(copy_segments(a, &segs, &dst_bytes));
+    if (segs.empty()) return C3_OK;
+    if (a.mover == C3_MOVER_CU) return copy_cu_enqueue(segs, a.opts, stream);
+    if (a.mover != C3_MOVER_SDMA) return fail(C3_E_INVALID, "unknown mover %d", a.mover);
+    C3_HIP_TRY(hipStreamSynchronize(stream));
+    SdmaOp op;
+    C3_TRY(sdma_issue(segs, a.opts, &op));
+    c3_timing t{};
+    return sdma_finish(&op, &t);
+}
+
+}  // namespace c3
+
+using namespace c3;
+
+#define C3_ENTRY(body)                                                      \
+    try {                                                                   \
+        std::lock_guard<std::recursive_mutex> lock_(api_mutex());           \
+        body                                                                \
+    } catch (const std::exception& e) {                                     \
+        return fail(C3_E_INVALID, "internal exception: %s", e.what());      \
+    } catch (...) {                                                         \
+        return fail(C3_E_INVALID, "internal exception");                    \
+    }
+
+extern "C" {
+
+c3_status c3_init(int hip_device) { C3_ENTRY(return init_device(hip_device);) }
+
+c3_status c3_finalize(void) {
+    C3_ENTRY(finalize_device(); return C3_OK;)
+}
+
+const char* c3_last_error(void) { return last_error_text(); }
+
+c3_status c3_device_info(c3_info* out) {
+    C3_ENTRY({
+        C3_TRY(require_init());
+        if (!out) return fail(C3_E_INVALID, "c3_device_info: out is NULL");
+        *out = ctx().info;
+        return C3_OK;
+    })
+}
+
+c3_status c3_stream_create(const uint32_t* cu_mask, int n_words, int priority, void** out) {
+    C3_ENTRY({
+        C3_TRY(require_init());
+        if (!out) return fail(C3_E_INVALID, "c3_stream_create: out is NULL");
+        if (priority != 0)
+            return fail(C3_E_UNSUPPORTED,
+                        "c3_stream_create: only default-priority streams are created "
+                        "(prioritize by issue order)");
+        if (n_words > 0 && !cu_mask) return fail(C3_E_INVALID, "c3_stream_create: mask is NULL");
+        hipStream_t s = nullptr;
+        C3_TRY(user_stream_create(cu_mask, n_words, &s));
+        *out = s;
+        return C3_OK;
+    })
+}
+
+c3_status c3_stream_destroy(void* stream) {
+    C3_ENTRY({
+        C3_TRY(require_init());
+        return user_stream_destroy(static_cast<hipStream_t>(stream));
+    })
+}
+
+c3_status c3_cu_mask_balanced(int keep_per_xcc, int complement, uint32_t* mask_out) {
+    C3_ENTRY({
+        C3_TRY(require_init());
+        if (!mask_out) return fail(C3_E_INVALID, "mask_out is NULL");
+        const c3_info& d = ctx().info;
+        const int per = d.n_cu / d.n_xcc;
+        if (keep_per_xcc < 1 || keep_per_xcc > per)
+            return fail(C3_E_INVALID, "keep_per_xcc must be in [1, %d]", per);
+        if (complement && keep_per_xcc == per)
+            return fail(C3_E_INVALID, "complement of a full mask is empty");
+        std::memset(mask_out, 0, sizeof(uint32_t) * C3_MAX_MASK_WORDS);
+        const int kept = keep_per_xcc * d.n_xcc;
+        for (int b = 0; b < d.n_cu && b < 32 * C3_MAX_MASK_WORDS; ++b) {
+            const bool in = b < kept;
+            if (in != (complement != 0)) mask_out[b / 32] |= 1u << (b % 32);
+        }
+        return C3_OK;
+    })
+}
+
+c3_status c3_probe_placement(void* stream, int n_blocks, uint32_t* out_dev) {
+    C3_ENTRY({
+        C3_TRY(require_init());
+        if (n_blocks < 1 || n_blocks > 65536)
+            return fail(C3_E_INVALID, "n_blocks must be in [1, 65536]");
+        C3_TRY(check_device_ptr(out_dev, (size_t)n_blocks * 8, "probe out"));
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        C3_TRY(probe_enqueue(n_blocks, out_dev, s));
+        C3_HIP_TRY(hipStreamSynchronize(s));
+        return C3_OK;
+    })
+}
+
+c3_status c3_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                  void* stream) {
+    C3_ENTRY({
+        C3_TRY(require_init());
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        GemmPlan plan;
+        C3_TRY(gemm_plan(A, B, C, M, N, K, s, &plan));
+        return gemm_enqueue(plan, s);
+    })
+}
+
+c3_status c3_gather(void* dst, const void* const* shards, int n_shards, size_t shard_bytes,
+                    c3_mover mover, const c3_move_opts* opt, void* stream) {
+    C3_ENTRY({
+        C3_TRY(require_init());
+        c3_copy_args a{};
+        a.kind = C3_COPY_GATHER;
+        a.mover = mover;
+        a.dst = dst;
+        a.shards = shards;
+        a.n_shards = n_shards;
+        a.shard_bytes = shard_bytes;
+        if (opt) a.opts = *opt;
+        return copy_isolated(a, static_cast<hipStream_t>(stream));
+    })
+}
+
+c3_status c3_all2all_block(void* dst, const void* src, int grid, size_t block_bytes,
+                           c3_mover mover, const c3_move_opts* opt, void* stream) {
+    C3_ENTRY({
+        C3_TRY(require_init());
+        c3_copy_args a{};
+        a.kind = C3_COPY_ALL2ALL;
+        a.mover = mover;
+        a.dst = dst;
+        a.src = src;
+        a.grid = grid;
+        a.block_bytes = block_bytes;
+        if (opt) a.opts = *opt;
+        return copy_isolated(a, static_cast<hipStream_t>(stream));
+    })
+}
+
+c3_status c3_flush_llc(size_t bytes, void* stream) {
+    C3_ENTRY({
+        C3_TRY(require_init());
+        if (bytes == 0) return C3_OK;
+        C3_TRY(ensure_flush_buffer(bytes));
+        return flush_enqueue(ctx().flush_buf, bytes, static_cast<hipStream_t>(stream));
+    })
+}
+
+c3_status c3_run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_conc_opts* o,
+                            c3_timing* t) {
+    C3_ENTRY({
+        C3_TRY(require_init());
+        return run_concurrent(g, c, o, t);
+    })
+}
+
+c3_status c3_derive_metrics(double t_gemm, double t_copy, double t_conc, double bytes_total,
+                            double bandwidth, c3_metrics* out) {
+    if (!out) return fail(C3_E_INVALID, "c3_derive_metrics: out is NULL");
+    if (!(t_gemm >= 0) || !(t_copy >= 0) || !(t_conc > 0) || !(std::max(t_gemm, t_copy) > 0))
+        return fail(C3_E_INVALID, "c3_derive_metrics: need t_gemm, t_copy >= 0, max > 0, t_conc > 0");
+    const double serial = t_gemm + t_copy;
+    const double longest = std::max(t_gemm, t_copy);
+    const double shortest = std::min(t_gemm, t_copy);
+    c3_metrics m{};
+    m.ideal_speedup = serial / longest;
+    m.speedup = serial / t_conc;
+    m.uplift_fraction = m.ideal_speedup == 1.0 ? std::nan("")
+                                               : (m.speedup - 1.0) / (m.ideal_speedup - 1.0);
+    m.ratio_of_ideal = m.speedup / m.ideal_speedup;
+    m.gemm_slowdown = t_gemm > 0 ? t_conc / t_gemm - 1.0 : std::nan("");
+    double floor_t = longest;
+    if (bytes_total > 0 && bandwidth > 0) floor_t = std::max(floor_t, bytes_total / bandwidth);
+    m.hbm_ceiling = serial / floor_t;
+    if (shortest > 0 && longest / shortest <= 1.15) m.taxonomy = C3_TAX_GC_EQUAL;
+    else m.taxonomy = t_gemm > t_copy ? C3_TAX_G_LONG : C3_TAX_C_LONG;
+    *out = m;
+    return C3_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// Internal declarations of libc3 (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hsa/hsa.h>
+#include <hsa/hsa_ext_amd.h>
+
+#include <cstdint>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "c3.h"
+
+namespace c3 {
+
+// ---- errors -------------------------------------------------------------------------------
+c3_status fail(c3_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+#define C3_HIP_TRY(call)                                                                      \
+    do {                                                                                      \
+        hipError_t e_ = (call);                                                               \
+        if (e_ != hipSuccess)                                                                 \
+            return ::c3::fail(C3_E_HIP, "%s failed: %s (%s:%d)", #call, hipGetErrorString(e_), \
+                              __FILE__, __LINE__);                                            \
+    } while (0)
+
+#define C3_HSA_TRY(call)                                                                      \
+    do {                                                                                      \
+        hsa_status_t s_ = (call);                                                             \
+        if (s_ != HSA_STATUS_SUCCESS) {                                                       \
+            const char* m_ = nullptr;                                                         \
+            hsa_status_string(s_, &m_);                                                       \
+            return ::c3::fail(C3_E_HSA, "%s failed: %s (%s:%d)", #call, m_ ? m_ : "?",        \
+                              __FILE__, __LINE__);                                            \
+        }                                                                                     \
+    } while (0)
+
+#define C3_TRY(expr)                      \
+    do {                                  \
+        c3_status st_ = (expr);           \
+        if (st_ != C3_OK) return st_;     \
+    } while (0)
+
+// ---- library state --------------------------------------------------------------------------
+struct Context {
+    bool inited = false;
+    int device = -1;
+    hsa_agent_t agent{};
+    c3_info info{};
+    std::vector<uint32_t> sdma_engines;  // one-hot engine ids usable for device-local copies
+    void* flush_buf = nullptr;
+    size_t flush_bytes = 0;
+};
+Context& ctx();
+std::recursive_mutex& api_mutex();
+c3_status require_init();
+
+// ---- argument checks --------------------------------------------------------------------------
+c3_status check_device_ptr(const void* p, size_t bytes, const char* what);
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb);
+
+// ---- GEMM (gemm.hip) ----------------------------------------------------------------------------
+struct GemmPlan {
+    const void* A = nullptr;
+    const void* B = nullptr;
+    void* C = nullptr;
+    int M = 0, N = 0, K = 0;
+    int kind = 0;          // 0 = 256x256 tile kernel, 1 = skinny split-K kernel
+    int splits = 1;        // skinny: K splits (1 = write bf16 directly)
+    int k_per_split = 0;
+    float* workspace = nullptr;  // skinny, splits > 1: fp32 partials [splits][Mpad][N]
+    size_t workspace_bytes = 0;
+};
+c3_status gemm_validate(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K);
+// Choose the kernel and (for split-K) make sure a workspace exists for `stream`. May allocate.
+c3_status gemm_plan(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                    hipStream_t stream, GemmPlan* plan);
+// Launch only (no allocation, no synchronization).
+c3_status gemm_enqueue(const GemmPlan& plan, hipStream_t stream);
+void gemm_release_workspaces();
+
+// ---- copies (copy.hip) ----------------------------------------------------------------------------
+struct Segment {
+    const void* src;
+    void* dst;
+    uint64_t bytes;
+};
+c3_status copy_cu_enqueue(const std::vector<Segment>& segs, const c3_move_opts& o,
+                          hipStream_t stream);
+c3_status flush_enqueue(void* buf, size_t bytes, hipStream_t stream);
+c3_status probe_enqueue(int n_blocks, uint32_t* out_dev, hipStream_t stream);
+
+// ---- SDMA (sdma.cpp) ----------------------------------------------------------------------------
+c3_status sdma_discover();
+void sdma_release();
+
+struct SdmaOp {
+    std::vector<hsa_signal_t> signals;  // one per chunk
+    std::vector<uint32_t> engine_of;    // engine id per chunk
+    std::vector<int> issued;            // 1 if the chunk was handed to ROCr
+    uint32_t engines_used = 0;
+    int fault_mode = 0;
+    int fault_chunk = -1;
+    int64_t deadline_ns = 0;
+};
+// Split segments into chunks and issue them on the engines (host returns right after issue).
+c3_status sdma_issue(const std::vector<Segment>& segs, const c3_move_opts& o, SdmaOp* op);
+// Nonblocking: true once every chunk's signal has left the "pending" state.
+bool sdma_done(const SdmaOp& op);
+// Wait for all chunks (bounded by the op's deadline), collect errors and timestamps, and return
+// the signals to the pool. Always waits for every chunk that was really issued.
+c3_status sdma_finish(SdmaOp* op, c3_timing* t);
+
+// ---- streams and timing (concurrent.cpp) ---------------------------------------------------------
+c3_status stream_for_mask(const uint32_t* mask, hipStream_t* out);
+void release_streams();
+int64_t now_ns();
+
+}  // namespace c3

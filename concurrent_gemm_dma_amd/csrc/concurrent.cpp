@@ -1,0 +1,317 @@
+// concurrent.cpp -- the C3 controller: CU-masked streams, issue order, completion and timing of
+// one GEMM running concurrently with one collective-shaped copy ("Optimizing ML Concurrent
+// Computation and Communication with GPU DMA Engines": abstract and Fig. 1 for the concurrent
+// run; Section IV-B3 for isolated times; Section V-B and Fig. 8 for schedule prioritization and
+// CU partitioning; Section VI-F for removing CUs from the GEMM when the copy runs on DMA).
+//
+// * Partitioning: the GEMM runs on a stream created with hipExtStreamCreateWithCUMask; a
+//   CU-mover copy runs on a second masked stream (typically the complement). Every library
+//   stream carries an explicit mask (all CUs when unrestricted) so that each gets a hardware
+//   queue of its own and the two operations can really overlap.
+// * Prioritization: the communication is issued before the GEMM (comm_first). Streams keep the
+//   default priority.
+// * Completion: the host polls the GEMM's end event and the copy's end event (CU mover) or
+//   completion signals (SDMA mover) and timestamps each completion on a monotonic clock.
+#include <algorithm>
+#include <array>
+#include <chrono>
+#include <cmath>
+#include <map>
+#include <set>
+
+#include "c3_internal.h"
+
+namespace c3 {
+
+int64_t now_ns() {
+    return std::chrono::duration_cast<std::chrono::nanoseconds>(
+               std::chrono::steady_clock::now().time_since_epoch())
+        .count();
+}
+
+namespace {
+
+using MaskKey = std::pair<int, std::array<uint32_t, C3_MAX_MASK_WORDS>>;
+
+std::map<MaskKey, hipStream_t>& stream_cache() {
+    static std::map<MaskKey, hipStream_t> m;
+    return m;
+}
+
+std::set<hipStream_t>& user_streams() {
+    static std::set<hipStream_t> s;
+    return s;
+}
+
+struct Events {
+    hipEvent_t g0 = nullptr, g1 = nullptr, c0 = nullptr, c1 = nullptr;
+};
+Events& events() {
+    static Events e;
+    return e;
+}
+
+int mask_words() { return std::max(1, (ctx().info.n_cu + 31) / 32); }
+
+// Normalise a mask: all-zero means every CU; bits beyond the device's CUs are dropped.
+std::array<uint32_t, C3_MAX_MASK_WORDS> normalise(const uint32_t* mask, int n_words) {
+    std::array<uint32_t, C3_MAX_MASK_WORDS> m{};
+    bool any = false;
+    for (int i = 0; i < n_words && i < C3_MAX_MASK_WORDS; ++i) {
+        m[i] = mask ? mask[i] : 0u;
+        any |= m[i] != 0;
+    }
+    const int n_cu = ctx().info.n_cu;
+    for (int b = 0; b < 32 * C3_MAX_MASK_WORDS; ++b) {
+        const bool in_device = b < n_cu;
+        uint32_t& w = m[b / 32];
+        const uint32_t bit = 1u << (b % 32);
+        if (!any) w = in_device ? (w | bit) : (w & ~bit);
+        else if (!in_device) w &= ~bit;
+    }
+    return m;
+}
+
+c3_status create_masked(const std::array<uint32_t, C3_MAX_MASK_WORDS>& m, hipStream_t* out) {
+    bool any = false;
+    for (uint32_t w : m) any |= w != 0;
+    if (!any) return fail(C3_E_INVALID, "CU mask selects no CU of this device");
+    C3_HIP_TRY(hipExtStreamCreateWithCUMask(out, (uint32_t)mask_words(), m.data()));
+    return C3_OK;
+}
+
+c3_status ensure_events() {
+    Events& e = events();
+    if (!e.g0) {
+        C3_HIP_TRY(hipEventCreate(&e.g0));
+        C3_HIP_TRY(hipEventCreate(&e.g1));
+        C3_HIP_TRY(hipEventCreate(&e.c0));
+        C3_HIP_TRY(hipEventCreate(&e.c1));
+    }
+    return C3_OK;
+}
+
+}  // namespace
+
+// role 0 = GEMM, 1 = communication: the two roles never share a stream, even with equal masks.
+c3_status stream_for_role(int role, const uint32_t* mask, hipStream_t* out) {
+    const auto m = normalise(mask, C3_MAX_MASK_WORDS);
+    const MaskKey key{role, m};
+    auto& cache = stream_cache();
+    auto it = cache.find(key);
+    if (it != cache.end()) {
+        *out = it->second;
+        return C3_OK;
+    }
+    hipStream_t s = nullptr;
+    C3_TRY(create_masked(m, &s));
+    cache[key] = s;
+    *out = s;
+    return C3_OK;
+}
+
+c3_status stream_for_mask(const uint32_t* mask, hipStream_t* out) { return stream_for_role(0, mask, out); }
+
+c3_status user_stream_create(const uint32_t* mask, int n_words, hipStream_t* out) {
+    if (n_words < 0 || n_words > C3_MAX_MASK_WORDS)
+        return fail(C3_E_INVALID, "n_words must be in [0, %d]", C3_MAX_MASK_WORDS);
+    const auto m = normalise(n_words ? mask : nullptr, n_words);
+    hipStream_t s = nullptr;
+    C3_TRY(create_masked(m, &s));
+    user_streams().insert(s);
+    *out = s;
+    return C3_OK;
+}
+
+c3_status user_stream_destroy(hipStream_t s) {
+    auto& us = user_streams();
+    if (!us.count(s)) return fail(C3_E_INVALID, "stream %p was not created by c3_stream_create", (void*)s);
+    us.erase(s);
+    C3_HIP_TRY(hipStreamDestroy(s));
+    return C3_OK;
+}
+
+void release_streams() {
+    for (auto& kv : stream_cache()) (void)hipStreamDestroy(kv.second);
+    stream_cache().clear();
+    for (hipStream_t s : user_streams()) (void)hipStreamDestroy(s);
+    user_streams().clear();
+    Events& e = events();
+    for (hipEvent_t* ev : {&e.g0, &e.g1, &e.c0, &e.c1})
+        if (*ev) {
+            (void)hipEventDestroy(*ev);
+            *ev = nullptr;
+        }
+}
+
+c3_status ensure_flush_buffer(size_t bytes) {
+    Context& c = ctx();
+    if (c.flush_bytes >= bytes) return C3_OK;
+    if (c.flush_buf) C3_HIP_TRY(hipFree(c.flush_buf));
+    c.flush_buf = nullptr;
+    c.flush_bytes = 0;
+    C3_HIP_TRY(hipMalloc(&c.flush_buf, bytes));
+    c.flush_bytes = bytes;
+    return C3_OK;
+}
+
+// Defined in abi.cpp: validate a copy description and turn it into segments.
+c3_status copy_segments(const c3_copy_args& a, std::vector<Segment>* segs, size_t* dst_bytes);
+
+c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_conc_opts* o_in,
+                         c3_timing* t_out) {
+    c3_conc_opts o{};
+    if (o_in) o = *o_in;
+    if (o.use_priority)
+        return fail(C3_E_UNSUPPORTED,
+                    "stream priorities are not used: every stream stays at default priority; "
+                    "prioritize with comm_first (issue order)");
+    if (!g && !c) return fail(C3_E_INVALID, "c3_run_concurrent: neither a GEMM nor a copy given");
+
+    // ---- validation and planning (may allocate; all before the clock starts) ----
+    GemmPlan plan;
+    hipStream_t gs = nullptr, cs = nullptr;
+    if (g) {
+        C3_TRY(stream_for_role(0, o.gemm_cu_mask, &gs));
+        C3_TRY(gemm_plan(g->A, g->B, g->C, g->M, g->N, g->K, gs, &plan));
+    }
+    std::vector<Segment> segs;
+    c3_move_opts mo{};
+    bool sdma = false;
+    if (c) {
+        size_t dst_bytes = 0;
+        C3_TRY(copy_segments(*c, &segs, &dst_bytes));
+        mo = c->opts;
+        if (c->mover == C3_MOVER_SDMA) {
+            sdma = true;
+        } else if (c->mover == C3_MOVER_CU) {
+            C3_TRY(stream_for_role(1, o.comm_cu_mask, &cs));
+        } else {
+            return fail(C3_E_INVALID, "unknown mover %d", c->mover);
+        }
+        if (g) {
+            const size_t a_b = (size_t)g->M * g->K * 2, b_b = (size_t)g->K * g->N * 2,
+                         c_b = (size_t)g->M * g->N * 2;
+            for (const Segment& s : segs) {
+                if (ranges_overlap(s.dst, s.bytes, g->A, a_b) ||
+                    ranges_overlap(s.dst, s.bytes, g->B, b_b) ||
+                    ranges_overlap(s.dst, s.bytes, g->C, c_b) ||
+                    ranges_overlap(s.src, s.bytes, g->C, c_b))
+                    return fail(C3_E_OVERLAP, "copy buffers overlap the GEMM's operands");
+            }
+        }
+    }
+    C3_TRY(ensure_events());
+    Events& ev = events();
+
+    // ---- idle device, optional last-level-cache flush ----
+    C3_HIP_TRY(hipDeviceSynchronize());
+    if (o.flush_bytes) {
+        C3_TRY(ensure_flush_buffer((size_t)o.flush_bytes));
+        C3_TRY(flush_enqueue(ctx().flush_buf, (size_t)o.flush_bytes, gs ? gs : cs));
+        C3_HIP_TRY(hipDeviceSynchronize());
+    }
+
+    // ---- issue ----
+    SdmaOp op;
+    c3_status gemm_st = C3_OK, copy_st = C3_OK;
+    bool copy_issued = false, gemm_issued = false;
+    auto issue_gemm = [&]() {
+        if (hipEventRecord(ev.g0, gs) != hipSuccess) {
+            gemm_st = fail(C3_E_HIP, "hipEventRecord failed");
+            return;
+        }
+        gemm_st = gemm_enqueue(plan, gs);
+        if (gemm_st == C3_OK && hipEventRecord(ev.g1, gs) != hipSuccess)
+            gemm_st = fail(C3_E_HIP, "hipEventRecord failed");
+        gemm_issued = gemm_st == C3_OK;
+    };
+    auto issue_copy = [&]() {
+        if (sdma) {
+            copy_st = sdma_issue(segs, mo, &op);
+        } else {
+            if (hipEventRecord(ev.c0, cs) != hipSuccess) {
+                copy_st = fail(C3_E_HIP, "hipEventRecord failed");
+                return;
+            }
+            copy_st = copy_cu_enqueue(segs, mo, cs);
+            if (copy_st == C3_OK && hipEventRecord(ev.c1, cs) != hipSuccess)
+                copy_st = fail(C3_E_HIP, "hipEventRecord failed");
+        }
+        copy_issued = copy_st == C3_OK;
+    };
+
+    const int64_t t0 = now_ns();
+    if (c && o.comm_first) issue_copy();
+    if (g) issue_gemm();
+    if (c && !o.comm_first) issue_copy();
+    const int64_t t_issue = now_ns() - t0;
+
+    // ---- poll for completion ----
+    bool gdone = !gemm_issued, cdone = !copy_issued;
+    int64_t tg = 0, tc = 0;
+    while (!(gdone && cdone)) {
+        if (!gdone) {
+            const hipError_t e = hipEventQuery(ev.g1);
+            if (e == hipSuccess) {
+                gdone = true;
+                tg = now_ns() - t0;
+            } else if (e != hipErrorNotReady) {
+                gemm_st = fail(C3_E_HIP, "GEMM completion query failed: %s", hipGetErrorString(e));
+                gdone = true;
+            }
+        }
+        if (!cdone) {
+            if (sdma) {
+                if (sdma_done(op)) {
+                    cdone = true;
+                    tc = now_ns() - t0;
+                } else if (now_ns() > op.deadline_ns) {
+                    cdone = true;  // sdma_finish reports the timeout
+                }
+            } else {
+                const hipError_t e = hipEventQuery(ev.c1);
+                if (e == hipSuccess) {
+                    cdone = true;
+                    tc = now_ns() - t0;
+                } else if (e != hipErrorNotReady) {
+                    copy_st = fail(C3_E_HIP, "copy completion query failed: %s", hipGetErrorString(e));
+                    cdone = true;
+                }
+            }
+        }
+    }
+    const int64_t t1 = now_ns();
+
+    c3_timing t{};
+    if (sdma && copy_issued) {
+        const c3_status st = sdma_finish(&op, &t);
+        if (st != C3_OK) copy_st = st;
+    }
+    // Make sure nothing is still running before returning (errors included).
+    if (gemm_issued) (void)hipEventSynchronize(ev.g1);
+    if (copy_issued && !sdma) (void)hipEventSynchronize(ev.c1);
+
+    t.t_conc_ns = t1 - t0;
+    t.t_gemm_done_ns = tg;
+    t.t_copy_done_ns = tc;
+    t.t_issue_ns = t_issue;
+    t.applied_priority = 0;
+    t.comm_issued_first = (c && o.comm_first) ? 1 : 0;
+    if (gemm_issued) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, ev.g0, ev.g1) == hipSuccess) t.gemm_gpu_ms = ms;
+    }
+    if (copy_issued && !sdma) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, ev.c0, ev.c1) == hipSuccess) t.copy_gpu_ms = ms;
+        t.n_chunks = (int32_t)segs.size();
+    }
+    if (t_out) *t_out = t;
+    if (gemm_st != C3_OK) return gemm_st;
+    if (copy_st != C3_OK) return copy_st;
+    C3_HIP_TRY(hipGetLastError());
+    return C3_OK;
+}
+
+}  // namespace c3

@@ -1,0 +1,201 @@
+// copy.hip -- the CU mover: collective-shaped copies done by compute-unit kernels, the way the
+// paper's baseline runs RCCL collectives on CUs ("Optimizing ML Concurrent Computation and
+// Communication with GPU DMA Engines", Section II-C and Fig. 1, c3_base). A collective's local
+// share is a list of (src, dst, bytes) segments: the 8 shards of an all-gather, or the 64 blocks
+// of an 8x8 all-to-all. Also: a last-level-cache flush and a CU placement probe.
+//
+// Vector path: every lane moves 16-byte pieces; a workgroup owns a contiguous run of pieces
+// across the concatenated segments, issues all of its loads before its stores (UNROLL pieces per
+// lane in flight), and a wavefront covers 1 KiB of contiguous bytes per access. Pieces that are
+// not 16-byte aligned on both sides, and segment tails shorter than 16 bytes, go to a byte path.
+#include "c3_internal.h"
+
+#include <algorithm>
+
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kSegPerLaunch = 64;
+constexpr int kThreads = 256;
+constexpr int kUnroll = 8;
+constexpr uint64_t kPiecesPerIter = (uint64_t)kThreads * kUnroll;  // 16-byte pieces
+
+struct SegTable {
+    uint64_t src[kSegPerLaunch];
+    uint64_t dst[kSegPerLaunch];
+    uint64_t first[kSegPerLaunch + 1];  // prefix sums of pieces: segment s owns [first[s], first[s+1])
+    int n;
+};
+
+__device__ __forceinline__ int find_segment(const SegTable& t, uint64_t piece) {
+    int lo = 0, hi = t.n - 1;  // largest s with first[s] <= piece
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (t.first[mid] <= piece) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void copy_pieces(const SegTable t, uint64_t pieces_per_block) {
+    const uint64_t total = t.first[t.n];
+    const uint64_t begin = (uint64_t)blockIdx.x * pieces_per_block;
+    const uint64_t end = min(total, begin + pieces_per_block);
+    int seg = find_segment(t, begin);
+    for (uint64_t base = begin; base < end; base += kPiecesPerIter) {
+        u32x4_t v[kUnroll];
+        u32x4_t* dptr[kUnroll];
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) {
+            const uint64_t piece = base + (uint64_t)i * kThreads + threadIdx.x;
+            dptr[i] = nullptr;
+            if (piece < end) {
+                int s = seg;
+                while (piece >= t.first[s + 1]) ++s;
+                const uint64_t off = (piece - t.first[s]) * 16u;
+                const u32x4_t* sp = reinterpret_cast<const u32x4_t*>(t.src[s] + off);
+                dptr[i] = reinterpret_cast<u32x4_t*>(t.dst[s] + off);
+                v[i] = NT ? __builtin_nontemporal_load(sp) : *sp;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kUnroll; ++i) {
+            if (dptr[i]) {
+                if (NT) __builtin_nontemporal_store(v[i], dptr[i]);
+                else *dptr[i] = v[i];
+            }
+        }
+        // segments only advance: start the next iteration's search from the first piece's one
+        const uint64_t next = base + kPiecesPerIter;
+        if (next < end)
+            while (next >= t.first[seg + 1]) ++seg;
+    }
+}
+
+// Byte path for misaligned segments and sub-16-byte tails: grid-stride over the bytes of one
+// segment per blockIdx.y.
+struct ByteTable {
+    uint64_t src[kSegPerLaunch];
+    uint64_t dst[kSegPerLaunch];
+    uint64_t bytes[kSegPerLaunch];
+    int n;
+};
+
+__global__ __launch_bounds__(kThreads) void copy_bytes(const ByteTable t) {
+    const int s = blockIdx.y;
+    if (s >= t.n) return;
+    const unsigned char* src = reinterpret_cast<const unsigned char*>(t.src[s]);
+    unsigned char* dst = reinterpret_cast<unsigned char*>(t.dst[s]);
+    const uint64_t n = t.bytes[s];
+    for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+         i += (uint64_t)gridDim.x * kThreads)
+        dst[i] = src[i];
+}
+
+__global__ __launch_bounds__(kThreads) void fill_pattern(u32x4_t* buf, uint64_t n16, uint32_t seed) {
+    const u32x4_t v = {seed, seed ^ 0x9E3779B9u, seed + 0x7F4A7C15u, ~seed};
+    for (uint64_t i = (uint64_t)blockIdx.x * kThreads + threadIdx.x; i < n16;
+         i += (uint64_t)gridDim.x * kThreads)
+        buf[i] = v;
+}
+
+// One wave per workgroup records HW_ID (wave, SIMD, CU, shader array and engine ids) and
+// XCC_ID, then stays resident for a few microseconds so later workgroups land on other CUs.
+__global__ __launch_bounds__(64) void placement_probe(uint32_t* out) {
+    const uint32_t hw = __builtin_amdgcn_s_getreg((4) | (0 << 6) | (31 << 11));    // HW_ID
+    const uint32_t xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | (31 << 11));  // XCC_ID
+    if (threadIdx.x == 0) {
+        out[2 * blockIdx.x] = hw;
+        out[2 * blockIdx.x + 1] = xcc;
+    }
+    const uint64_t t0 = __builtin_readcyclecounter();
+    while (__builtin_readcyclecounter() - t0 < 40000) {
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+}  // namespace
+
+namespace c3 {
+
+c3_status copy_cu_enqueue(const std::vector<Segment>& segs, const c3_move_opts& o,
+                          hipStream_t stream) {
+    // Split every segment into a 16-byte-aligned body (vector path) and the rest (byte path).
+    std::vector<Segment> vec, bytes;
+    for (const Segment& s : segs) {
+        if (s.bytes == 0) continue;
+        const bool aligned = (((uintptr_t)s.src | (uintptr_t)s.dst) & 15) == 0;
+        const uint64_t body = aligned ? (s.bytes & ~15ull) : 0;
+        if (body) vec.push_back({s.src, s.dst, body});
+        if (body < s.bytes)
+            bytes.push_back({static_cast<const char*>(s.src) + body, static_cast<char*>(s.dst) + body,
+                             s.bytes - body});
+    }
+    for (size_t b = 0; b < vec.size(); b += kSegPerLaunch) {
+        SegTable t{};
+        t.n = (int)std::min<size_t>(kSegPerLaunch, vec.size() - b);
+        uint64_t acc = 0;
+        for (int i = 0; i < t.n; ++i) {
+            t.src[i] = (uint64_t)(uintptr_t)vec[b + i].src;
+            t.dst[i] = (uint64_t)(uintptr_t)vec[b + i].dst;
+            t.first[i] = acc;
+            acc += vec[b + i].bytes / 16;
+        }
+        t.first[t.n] = acc;
+        uint64_t blocks;
+        uint64_t per_block;
+        if (o.cu_blocks > 0) {
+            blocks = (uint64_t)o.cu_blocks;
+            per_block = (acc + blocks - 1) / blocks;
+            per_block = (per_block + kPiecesPerIter - 1) / kPiecesPerIter * kPiecesPerIter;
+        } else {
+            per_block = 4096;  // 64 KiB per workgroup
+        }
+        blocks = (acc + per_block - 1) / per_block;
+        if (blocks > 0x7FFFFFFFull) return fail(C3_E_INVALID, "copy too large for one launch");
+        if (o.nontemporal)
+            hipLaunchKernelGGL(copy_pieces<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, t,
+                               per_block);
+        else
+            hipLaunchKernelGGL(copy_pieces<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, t,
+                               per_block);
+        C3_HIP_TRY(hipGetLastError());
+    }
+    for (size_t b = 0; b < bytes.size(); b += kSegPerLaunch) {
+        ByteTable t{};
+        t.n = (int)std::min<size_t>(kSegPerLaunch, bytes.size() - b);
+        uint64_t longest = 0;
+        for (int i = 0; i < t.n; ++i) {
+            t.src[i] = (uint64_t)(uintptr_t)bytes[b + i].src;
+            t.dst[i] = (uint64_t)(uintptr_t)bytes[b + i].dst;
+            t.bytes[i] = bytes[b + i].bytes;
+            longest = std::max(longest, t.bytes[i]);
+        }
+        const unsigned gx = (unsigned)std::min<uint64_t>(1024, (longest + kThreads - 1) / kThreads);
+        hipLaunchKernelGGL(copy_bytes, dim3(gx, t.n), dim3(kThreads), 0, stream, t);
+        C3_HIP_TRY(hipGetLastError());
+    }
+    return C3_OK;
+}
+
+c3_status flush_enqueue(void* buf, size_t bytes, hipStream_t stream) {
+    const uint64_t n16 = bytes / 16;
+    if (!n16) return C3_OK;
+    static uint32_t seed = 0x1234567u;
+    seed = seed * 1664525u + 1013904223u;
+    const unsigned blocks = (unsigned)std::min<uint64_t>(8192, (n16 + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(fill_pattern, dim3(blocks), dim3(kThreads), 0, stream,
+                       static_cast<u32x4_t*>(buf), n16, seed);
+    C3_HIP_TRY(hipGetLastError());
+    return C3_OK;
+}
+
+c3_status probe_enqueue(int n_blocks, uint32_t* out_dev, hipStream_t stream) {
+    hipLaunchKernelGGL(placement_probe, dim3(n_blocks), dim3(64), 0, stream, out_dev);
+    C3_HIP_TRY(hipGetLastError());
+    return C3_OK;
+}
+
+}  // namespace c3

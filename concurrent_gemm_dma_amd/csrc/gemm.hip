@@ -1,0 +1,537 @@
+// gemm.hip -- bf16 GEMM C[M][N] = A[M][K] . B[K][N] for gfx950 (CDNA4), fp32 accumulation,
+// round-to-nearest-even bf16 result. Row-major operands, no alpha/beta.
+//
+// The paper's computation is the GEMM of LLaMA-class training layers ("Optimizing ML Concurrent
+// Computation and Communication with GPU DMA Engines", Section IV, Fig. 5a). Two kernels:
+//
+// * tile256: 256x256 output tile per workgroup, K step 64, 4 waves (2x2), each wave 128x128
+//   built from 4x4 v_mfma_f32_32x32x16_bf16. Operands are staged global -> registers -> LDS
+//   (double-buffered, one barrier per K step). The MFMA is fed transposed (B^T as the row
+//   operand, A^T as the column operand), so each lane's accumulators are 4 consecutive columns
+//   of one C row and the epilogue writes 8-byte runs. B stays K x N in LDS and is read with the
+//   LDS transpose load (ds_read_b64_tr_b16), which hands each lane 4 consecutive k of one
+//   column. Compute-bound shapes use this kernel.
+// * skinny: 16 x 256 tile, K split across workgroups (deterministic: fp32 partials per split,
+//   summed in split order by a second kernel), v_mfma_f32_16x16x32_bf16. For M <= 64, where the
+//   GEMM streams B once and is bound by HBM bandwidth.
+//
+// Global loads and C stores use raw buffer instructions whose resource covers only the valid
+// part of the operand: anything past it reads as zero / is dropped, and ragged M, N, K edges are
+// masked explicitly by pointing the lane at an out-of-range offset.
+#include "c3_internal.h"
+
+#include <algorithm>
+#include <cstdlib>
+#include <map>
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define C3_LDS __attribute__((address_space(3)))
+
+// Raw buffer resource word 3 for gfx9-family parts (32-bit data format, no swizzle, no stride).
+constexpr int kRsrcWord3 = 0x00020000;
+// Any offset >= the resource's record count reads zero / drops the store.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr uint64_t kMaxRecords = 0x7FFFFFF0ull;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    uint64_t n = bytes <= 0 ? 0ull : (uint64_t)bytes;
+    if (n > kMaxRecords) n = kMaxRecords;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ void store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2_t v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+
+__device__ __forceinline__ void lds_store16(char* lds, uint32_t off, u32x4_t v) {
+    *reinterpret_cast<C3_LDS u32x4_t*>((C3_LDS char*)lds + off) = v;
+}
+
+__device__ __forceinline__ bf16x8_t lds_load16(const char* lds, uint32_t off) {
+    return *reinterpret_cast<const C3_LDS bf16x8_t*>((const C3_LDS char*)lds + off);
+}
+
+// Two LDS transpose loads (4 k each) form one 8-k MFMA row operand.
+__device__ __forceinline__ bf16x8_t lds_load_tr8(const char* lds, uint32_t off_lo,
+                                                 uint32_t off_hi) {
+    i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<C3_LDS i16x4_t*>((C3_LDS char*)lds + off_lo));
+    i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        reinterpret_cast<C3_LDS i16x4_t*>((C3_LDS char*)lds + off_hi));
+    i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Round 4 fp32 to bf16 (nearest even; v_cvt_pk_bf16_f32) and pack.
+__device__ __forceinline__ u32x2_t pack_bf16x4(float a, float b, float c, float d) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t p0 = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    bf16x2_t p1 = {static_cast<__bf16>(c), static_cast<__bf16>(d)};
+    u32x2_t r;
+    r.x = __builtin_bit_cast(uint32_t, p0);
+    r.y = __builtin_bit_cast(uint32_t, p1);
+    return r;
+}
+
+// LDS swizzles (16-byte chunk index XOR), chosen so the MFMA operand reads below touch distinct
+// banks both when the LDS serves 16 lanes x 8 B (32 banks) and 32 lanes x 8 B (64 banks) per
+// cycle.
+// A tiles: rows of 64 k (128 B = 8 chunks); chunk ^= (row & 7) ^ bit 3 of row.
+__device__ __forceinline__ int swz_a(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// B tiles: rows of 256 n (512 B = 32 chunks); chunk ^= f(row & 3), f = {0, 6, 10, 12}.
+__device__ __forceinline__ int swz_b(int krow) {
+    const int r = krow & 3;
+    return (r << 2) ^ (((r ^ (r >> 1)) & 1) << 1);
+}
+
+// Workgroup -> output tile. The dispatcher places workgroup b on XCD (b mod 8); renumber so that
+// each XCD gets a contiguous range of logical tiles, then walk tiles in groups of GROUP_M tile
+// rows so that the tiles resident at one time on an XCD share A rows and B columns in its L2.
+template <int GROUP_M>
+__device__ __forceinline__ void map_tile(int bid, int nblocks, int tiles_m, int tiles_n, int& tm,
+                                         int& tn) {
+    int logical = bid;
+    if (nblocks >= 8) {
+        const int q = nblocks >> 3, rem = nblocks & 7;
+        const int x = bid & 7, local = bid >> 3;
+        logical = x * q + (x < rem ? x : rem) + local;
+    }
+    const int per_group = GROUP_M * tiles_n;
+    const int group = logical / per_group;
+    const int first_m = group * GROUP_M;
+    const int gm = min(tiles_m - first_m, GROUP_M);
+    const int in_group = logical - group * per_group;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+}
+
+// ------------------------------------------------------------------------------------------------
+// 256 x 256 tile kernel
+// ------------------------------------------------------------------------------------------------
+namespace t256 {
+constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
+constexpr int A_STAGE = BM * BK * 2;  // 32 KiB
+constexpr int B_STAGE = BK * BN * 2;  // 32 KiB
+constexpr int STAGE = A_STAGE + B_STAGE;
+constexpr int A_LD = BM * BK / 8 / NT;  // 16-byte chunks per thread per stage: 8
+constexpr int B_LD = BK * BN / 8 / NT;  // 8
+constexpr int GROUP_M = 8;
+}  // namespace t256
+
+__global__ __launch_bounds__(256, 1) void gemm_bf16_tile256(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
+    int M, int N, int K, int tiles_m, int tiles_n) {
+    using namespace t256;
+    __shared__ __attribute__((aligned(128))) char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int tm, tn;
+    map_tile<GROUP_M>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // ---- global -> register addressing (per thread: 8 A chunks, 8 B chunks per stage) ----
+    // A chunk i of this thread: row i*32 + tid/8, k chunk tid%8.
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + (size_t)m0 * K, (int64_t)(M - m0) * K * 2);
+    const int a_row = tid >> 3, a_kc = tid & 7;
+    const uint32_t a_g0 = (uint32_t)a_row * (uint32_t)K * 2u + (uint32_t)a_kc * 16u;
+    const uint32_t a_gstep = 32u * (uint32_t)K * 2u;
+    const uint32_t a_s0 = (uint32_t)a_row * 128u + (uint32_t)((a_kc ^ swz_a(a_row)) << 4);
+    // B chunk i of this thread: k row i*8 + tid/32, n chunk tid%32.
+    const int b_row = tid >> 5, b_nc = tid & 31;
+    const bool b_nvalid = (n0 + b_nc * 8) < N;
+    const uint32_t b_g0 = (uint32_t)b_row * (uint32_t)N * 2u + (uint32_t)b_nc * 16u;
+    const uint32_t b_gstep = 8u * (uint32_t)N * 2u;
+    const uint32_t b_s0 = (uint32_t)b_row * 512u + (uint32_t)((b_nc ^ swz_b(b_row)) << 4);
+
+    // ---- LDS -> MFMA operand addressing ----
+    // Column operand (A^T): lane reads row wm*128 + mi*32 + lane%32, k chunk kk*2 + lane/32.
+    const int ar = lane & 31;
+    const int a_sw = swz_a(ar);  // bits 0..3 of the row equal those of lane%32
+    uint32_t a_rd[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+        a_rd[kk] = (uint32_t)(wm * 128 + ar) * 128u +
+                   (uint32_t)((((kk * 2) + (lane >> 5)) ^ a_sw) << 4);
+    // Row operand (B^T) via transpose loads: lane (group G = lane/16, p = lane%16) supplies
+    // 4 n-contiguous bf16 of k row 8*(G/2) + p/4 (+16*kk, +4*h) at n = 32*ni + 16*(G%2) + 4*(p%4)
+    // of this wave's 128 columns; the load hands lane p column p of that 4 x 16 block.
+    const int G = lane >> 4, p = lane & 15;
+    const int b_krow = 8 * (G >> 1) + (p >> 2);
+    const int b_sw = swz_b(p >> 2);
+    uint32_t b_rd[4];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+        const int nc = wn * 16 + ni * 4 + 2 * (G & 1) + ((p >> 1) & 1);
+        b_rd[ni] = (uint32_t)b_krow * 512u + (uint32_t)((nc ^ b_sw) << 4) + (uint32_t)((p & 1) * 8);
+    }
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x16_t{};
+
+    u32x4_t ra[A_LD], rb[B_LD];
+
+    auto load_stage = [&](int k0) {
+        const bool a_kvalid = (k0 + a_kc * 8) < K;
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i)
+            ra[i] = load16(rA, a_kvalid ? a_g0 + (uint32_t)i * a_gstep + (uint32_t)k0 * 2u : kOOB);
+        const __amdgpu_buffer_rsrc_t rB =
+            make_rsrc(B + (size_t)k0 * N + n0, ((int64_t)(K - k0) * N - n0) * 2);
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i)
+            rb[i] = load16(rB, b_nvalid ? b_g0 + (uint32_t)i * b_gstep : kOOB);
+    };
+    auto store_stage = [&](int s) {
+        char* As = smem + s * STAGE;
+        char* Bs = As + A_STAGE;
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i) lds_store16(As, a_s0 + (uint32_t)i * 4096u, ra[i]);
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i) lds_store16(Bs, b_s0 + (uint32_t)i * 4096u, rb[i]);
+    };
+    auto compute_stage = [&](int s) {
+        const char* As = smem + s * STAGE;
+        const char* Bs = As + A_STAGE;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            bf16x8_t colop[4], rowop[4];
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) colop[mi] = lds_load16(As, a_rd[kk] + mi * 4096u);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                rowop[ni] = lds_load_tr8(Bs, b_rd[ni] + kk * 8192u, b_rd[ni] + kk * 8192u + 2048u);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 4; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowop[ni], colop[mi],
+                                                                          acc[mi][ni], 0, 0, 0);
+        }
+    };
+
+    const int nk = (K + BK - 1) / BK;
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) load_stage((kt + 1) * BK);
+        compute_stage(cur);
+        if (kt + 1 < nk) store_stage(cur ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane holds C[m][n..n+3], m = mi*32 + lane%32, n = ni*32 + 8g + 4*(lane/32)
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(C + (size_t)m0 * N + n0, ((int64_t)(M - m0) * N - n0) * 2);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int ml = wm * 128 + mi * 32 + (lane & 31);
+        const bool mvalid = (m0 + ml) < M;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nl = wn * 128 + ni * 32 + 8 * g + 4 * (lane >> 5);
+                const bool ok = mvalid && (n0 + nl) < N;
+                const uint32_t off = ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 2u : kOOB;
+                const f32x16_t& a = acc[mi][ni];
+                store8(rC, off, pack_bf16x4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]));
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Skinny (small M) split-K kernel
+// ------------------------------------------------------------------------------------------------
+namespace sk {
+constexpr int BM = 16, BN = 256, BK = 64, NT = 256;
+constexpr int A_STAGE = BM * BK * 2;  // 2 KiB
+constexpr int B_STAGE = BK * BN * 2;  // 32 KiB
+constexpr int STAGE = A_STAGE + B_STAGE;
+constexpr int B_LD = BK * BN / 8 / NT;  // 8
+}  // namespace sk
+
+// grid: x = N tiles of 256, y = K splits, z = M tiles of 16. Each workgroup covers k in
+// [y*k_per_split, min(K, (y+1)*k_per_split)). With splits == 1 it writes bf16 C; otherwise fp32
+// partials to ws[y][m][n] (m < Mpad = 16*gridDim.z).
+__global__ __launch_bounds__(256, 2) void gemm_bf16_skinny(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
+    float* __restrict__ ws, int M, int N, int K, int k_per_split) {
+    using namespace sk;
+    __shared__ __attribute__((aligned(128))) char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int n0 = blockIdx.x * BN;
+    const int m0 = blockIdx.z * BM;
+    const int kbeg = blockIdx.y * k_per_split;
+    const int kend = min(K, kbeg + k_per_split);
+
+    // A: 128 chunks (16 rows x 8), threads 0..127 load one each.
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + (size_t)m0 * K, (int64_t)(M - m0) * K * 2);
+    const int a_row = (tid >> 3) & 15, a_kc = tid & 7;
+    const bool a_loader = tid < 128;
+    const uint32_t a_g0 = (uint32_t)a_row * (uint32_t)K * 2u + (uint32_t)a_kc * 16u;
+    const uint32_t a_s0 = (uint32_t)a_row * 128u + (uint32_t)((a_kc ^ swz_a(a_row)) << 4);
+    // B: same 64 x 256 stage layout as the tile kernel.
+    const int b_row = tid >> 5, b_nc = tid & 31;
+    const bool b_nvalid = (n0 + b_nc * 8) < N;
+    const uint32_t b_g0 = (uint32_t)b_row * (uint32_t)N * 2u + (uint32_t)b_nc * 16u;
+    const uint32_t b_gstep = 8u * (uint32_t)N * 2u;
+    const uint32_t b_s0 = (uint32_t)b_row * 512u + (uint32_t)((b_nc ^ swz_b(b_row)) << 4);
+
+    // Column operand (A^T, 16 x 32 per MFMA): lane reads row lane%16, k chunk kk*4 + lane/16.
+    const int ar = lane & 15;
+    uint32_t a_rd[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+        a_rd[kk] = (uint32_t)ar * 128u + (uint32_t)((((kk * 4) + (lane >> 4)) ^ swz_a(ar)) << 4);
+    // Row operand (B^T, 16 n x 32 k): lane group G supplies k rows 8G + p/4 (+4h, +32kk),
+    // n = 64*wave + 16*ni + 4*(p%4).
+    const int G = lane >> 4, p = lane & 15;
+    const int b_sw = swz_b(p >> 2);
+    uint32_t b_rd[4];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+        const int nc = wave * 8 + ni * 2 + ((p >> 1) & 1);
+        b_rd[ni] = (uint32_t)(8 * G + (p >> 2)) * 512u + (uint32_t)((nc ^ b_sw) << 4) +
+                   (uint32_t)((p & 1) * 8);
+    }
+
+    f32x4_t acc[4];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[ni] = f32x4_t{};
+
+    u32x4_t ra, rb[B_LD];
+    auto load_stage = [&](int k0) {
+        const bool a_kvalid = a_loader && (k0 + a_kc * 8) < kend;
+        ra = load16(rA, a_kvalid ? a_g0 + (uint32_t)k0 * 2u : kOOB);
+        const __amdgpu_buffer_rsrc_t rB =
+            make_rsrc(B + (size_t)k0 * N + n0, ((int64_t)(kend - k0) * N - n0) * 2);
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i)
+            rb[i] = load16(rB, b_nvalid ? b_g0 + (uint32_t)i * b_gstep : kOOB);
+    };
+    auto store_stage = [&](int s) {
+        char* As = smem + s * STAGE;
+        char* Bs = As + A_STAGE;
+        if (a_loader) lds_store16(As, a_s0, ra);
+#pragma unroll
+        for (int i = 0; i < B_LD; ++i) lds_store16(Bs, b_s0 + (uint32_t)i * 4096u, rb[i]);
+    };
+    auto compute_stage = [&](int s) {
+        const char* As = smem + s * STAGE;
+        const char* Bs = As + A_STAGE;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8_t colop = lds_load16(As, a_rd[kk]);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const bf16x8_t rowop = lds_load_tr8(Bs, b_rd[ni] + kk * 16384u,
+                                                    b_rd[ni] + kk * 16384u + 2048u);
+                acc[ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rowop, colop, acc[ni], 0, 0, 0);
+            }
+        }
+    };
+
+    const int nk = (kend - kbeg + BK - 1) / BK;
+    if (nk > 0) {
+        load_stage(kbeg);
+        store_stage(0);
+        __syncthreads();
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            if (kt + 1 < nk) load_stage(kbeg + (kt + 1) * BK);
+            compute_stage(cur);
+            if (kt + 1 < nk) store_stage(cur ^ 1);
+            __syncthreads();
+        }
+    }
+
+    // lane holds D[n][m] for m = lane%16, n = 64*wave + 16*ni + 4*(lane/16) + v
+    const int ml = lane & 15;
+    const bool mvalid = (m0 + ml) < M;
+    if (gridDim.y == 1) {
+        const __amdgpu_buffer_rsrc_t rC =
+            make_rsrc(C + (size_t)m0 * N + n0, ((int64_t)(M - m0) * N - n0) * 2);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int nl = wave * 64 + ni * 16 + 4 * (lane >> 4);
+            const bool ok = mvalid && (n0 + nl) < N;
+            const uint32_t off = ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 2u : kOOB;
+            store8(rC, off, pack_bf16x4(acc[ni][0], acc[ni][1], acc[ni][2], acc[ni][3]));
+        }
+    } else {
+        const int mpad = gridDim.z * BM;
+        float* wsb = ws + ((size_t)blockIdx.y * mpad + m0) * N + n0;
+        const __amdgpu_buffer_rsrc_t rW = make_rsrc(wsb, ((int64_t)(mpad - m0) * N - n0) * 4);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const int nl = wave * 64 + ni * 16 + 4 * (lane >> 4);
+            const bool ok = (n0 + nl) < N;
+            const uint32_t off = ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 4u : kOOB;
+            store16(rW, off, __builtin_bit_cast(u32x4_t, acc[ni]));
+        }
+    }
+}
+
+// C[m][n..n+3] = bf16(sum over splits s = 0, 1, ... of ws[s][m][n..n+3]), in that order.
+__global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ ws,
+                                                    uint16_t* __restrict__ C, int M, int N,
+                                                    int mpad, int splits) {
+    const int nq = N >> 2;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)M * nq) return;
+    const int m = (int)(idx / nq);
+    const int n = (int)(idx - (int64_t)m * nq) * 4;
+    f32x4_t s = *reinterpret_cast<const f32x4_t*>(ws + (size_t)m * N + n);
+    for (int k = 1; k < splits; ++k)
+        s += *reinterpret_cast<const f32x4_t*>(ws + ((size_t)k * mpad + m) * N + n);
+    *reinterpret_cast<u32x2_t*>(C + (size_t)m * N + n) = pack_bf16x4(s[0], s[1], s[2], s[3]);
+}
+
+constexpr int64_t kMaxDim = 1 << 21;
+
+struct Workspace {
+    float* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::map<hipStream_t, Workspace>& workspaces() {
+    static std::map<hipStream_t, Workspace> w;
+    return w;
+}
+
+int env_int(const char* name, int dflt) {
+    const char* v = std::getenv(name);
+    return (v && *v) ? std::atoi(v) : dflt;
+}
+
+}  // namespace
+
+namespace c3 {
+
+c3_status gemm_validate(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K) {
+    if (!A || !B || !C) return fail(C3_E_INVALID, "c3_gemm: null operand pointer");
+    if (M < 1 || N < 1 || K < 1 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return fail(C3_E_INVALID, "c3_gemm: M, N, K must be in [1, %lld] (got %lld, %lld, %lld)",
+                    (long long)kMaxDim, (long long)M, (long long)N, (long long)K);
+    if (K % 8 || N % 8)
+        return fail(C3_E_INVALID, "c3_gemm: K and N must be multiples of 8 (got K=%lld N=%lld)",
+                    (long long)K, (long long)N);
+    if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)C) & 15)
+        return fail(C3_E_INVALID, "c3_gemm: A, B, C must be 16-byte aligned");
+    const size_t a_bytes = (size_t)M * K * 2, b_bytes = (size_t)K * N * 2, c_bytes = (size_t)M * N * 2;
+    C3_TRY(check_device_ptr(A, a_bytes, "A"));
+    C3_TRY(check_device_ptr(B, b_bytes, "B"));
+    C3_TRY(check_device_ptr(C, c_bytes, "C"));
+    if (ranges_overlap(A, a_bytes, C, c_bytes) || ranges_overlap(B, b_bytes, C, c_bytes))
+        return fail(C3_E_OVERLAP, "c3_gemm: C overlaps A or B");
+    return C3_OK;
+}
+
+c3_status gemm_plan(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                    hipStream_t stream, GemmPlan* plan) {
+    C3_TRY(gemm_validate(A, B, C, M, N, K));
+    GemmPlan p;
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    if (M <= 64) {
+        p.kind = 1;
+        const int tiles = (int)((N + sk::BN - 1) / sk::BN) * (int)((M + sk::BM - 1) / sk::BM);
+        const int n_cu = ctx().info.n_cu > 0 ? ctx().info.n_cu : 256;
+        int splits = env_int("C3_SKINNY_SPLITS", 0);
+        if (splits <= 0) splits = (2 * n_cu + tiles - 1) / tiles;
+        const int max_splits = std::max(1, (int)(K / (4 * sk::BK)));
+        splits = std::max(1, std::min(splits, max_splits));
+        int kps = (int)((K + splits - 1) / splits);
+        kps = (kps + sk::BK - 1) / sk::BK * sk::BK;
+        splits = (int)((K + kps - 1) / kps);
+        p.splits = splits;
+        p.k_per_split = kps;
+        if (splits > 1) {
+            const size_t mpad = (size_t)((M + sk::BM - 1) / sk::BM) * sk::BM;
+            const size_t need = (size_t)splits * mpad * (size_t)N * sizeof(float);
+            Workspace& w = workspaces()[stream];
+            if (w.bytes < need) {
+                if (w.ptr) C3_HIP_TRY(hipFree(w.ptr));
+                w.ptr = nullptr;
+                w.bytes = 0;
+                C3_HIP_TRY(hipMalloc(&w.ptr, need));
+                w.bytes = need;
+            }
+            p.workspace = w.ptr;
+            p.workspace_bytes = need;
+        }
+    } else {
+        p.kind = 0;
+    }
+    *plan = p;
+    return C3_OK;
+}
+
+c3_status gemm_enqueue(const GemmPlan& p, hipStream_t stream) {
+    const auto* A = static_cast<const uint16_t*>(p.A);
+    const auto* B = static_cast<const uint16_t*>(p.B);
+    auto* C = static_cast<uint16_t*>(p.C);
+    if (p.kind == 0) {
+        const int tiles_m = (p.M + t256::BM - 1) / t256::BM;
+        const int tiles_n = (p.N + t256::BN - 1) / t256::BN;
+        hipLaunchKernelGGL(gemm_bf16_tile256, dim3(tiles_m * tiles_n), dim3(t256::NT), 0, stream,
+                           A, B, C, p.M, p.N, p.K, tiles_m, tiles_n);
+        C3_HIP_TRY(hipGetLastError());
+        return C3_OK;
+    }
+    const int tiles_n = (p.N + sk::BN - 1) / sk::BN;
+    const int tiles_m = (p.M + sk::BM - 1) / sk::BM;
+    if (p.splits > 1 && !p.workspace) return fail(C3_E_INVALID, "split-K plan without workspace");
+    hipLaunchKernelGGL(gemm_bf16_skinny, dim3(tiles_n, p.splits, tiles_m), dim3(sk::NT), 0, stream,
+                       A, B, C, p.workspace, p.M, p.N, p.K, p.k_per_split);
+    C3_HIP_TRY(hipGetLastError());
+    if (p.splits > 1) {
+        const int64_t quads = (int64_t)p.M * (p.N / 4);
+        const int blocks = (int)((quads + 255) / 256);
+        hipLaunchKernelGGL(splitk_reduce, dim3(blocks), dim3(256), 0, stream, p.workspace, C, p.M,
+                           p.N, tiles_m * sk::BM, p.splits);
+        C3_HIP_TRY(hipGetLastError());
+    }
+    return C3_OK;
+}
+
+void gemm_release_workspaces() {
+    for (auto& kv : workspaces())
+        if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+    workspaces().clear();
+}
+
+}  // namespace c3

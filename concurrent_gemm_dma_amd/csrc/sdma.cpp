@@ -1,0 +1,303 @@
+// sdma.cpp -- the SDMA mover: a collective's local share moved by the GPU's system DMA engines,
+// which use no compute units and bypass the L1/L2 caches ("Optimizing ML Concurrent Computation
+// and Communication with GPU DMA Engines", Sections II-A and VI-A). As in the paper's ConCCL
+// proof-of-concepts (Section VI-B), the collective is split into individual transfers and each
+// transfer is put on an engine from the CPU with hsa_amd_memory_async_copy_on_engine.
+//
+// Design on gfx950:
+// * Engines: for a copy from a GPU to itself the copy-engine status call may report no engine,
+//   so the candidates are one engine id per SDMA engine the agent counts, and each candidate is
+//   kept only if a probe copy on it completes byte-exact at initialisation. Chunk c goes to
+//   engine list[c mod n] (round robin), so with the default of one chunk per shard or block the
+//   8 shards of an all-gather spread over the engines.
+// * force_copy_on_sdma = true on every call: for a same-device copy ROCr would otherwise use a
+//   blit kernel, i.e. compute units, which would defeat the purpose.
+// * One completion signal per chunk (initial value 1, decremented to 0 by the engine, negative
+//   on error), drawn from a pool, so that per-chunk engine timestamps
+//   (hsa_amd_profiling_get_async_copy_time) can be read back as evidence of overlap.
+// * The host issues and returns; completion is polled (sdma_done) or waited for (sdma_finish)
+//   with a deadline. A chunk that was really issued is always waited for before its signal is
+//   reused or an error is returned, so no engine can still be writing after a call returns,
+//   unless the engine itself hangs (then the signal is leaked, never reused).
+#include <algorithm>
+#include <chrono>
+#include <cstdlib>
+#include <cstring>
+
+#include "c3_internal.h"
+
+namespace c3 {
+namespace {
+
+std::vector<hsa_signal_t>& signal_pool() {
+    static std::vector<hsa_signal_t> pool;
+    return pool;
+}
+
+c3_status get_signal(hsa_signal_t* out) {
+    auto& pool = signal_pool();
+    if (!pool.empty()) {
+        *out = pool.back();
+        pool.pop_back();
+        return C3_OK;
+    }
+    C3_HSA_TRY(hsa_signal_create(1, 0, nullptr, out));
+    return C3_OK;
+}
+
+void put_signal(hsa_signal_t s) { signal_pool().push_back(s); }
+
+uint64_t system_tick_hz() {
+    static uint64_t hz = 0;
+    if (!hz) {
+        uint64_t f = 0;
+        if (hsa_system_get_info(HSA_SYSTEM_INFO_TIMESTAMP_FREQUENCY, &f) == HSA_STATUS_SUCCESS && f)
+            hz = f;
+        else
+            hz = 1000000000ull;
+    }
+    return hz;
+}
+
+bool profiling_on = false;
+
+}  // namespace
+
+c3_status sdma_discover() {
+    Context& c = ctx();
+    uint32_t n = 0;
+    if (hsa_agent_get_info(c.agent, (hsa_agent_info_t)HSA_AMD_AGENT_INFO_NUM_SDMA_ENG, &n) ==
+        HSA_STATUS_SUCCESS)
+        c.info.n_sdma = (int32_t)n;
+    n = 0;
+    if (hsa_agent_get_info(c.agent, (hsa_agent_info_t)HSA_AMD_AGENT_INFO_NUM_SDMA_XGMI_ENG, &n) ==
+        HSA_STATUS_SUCCESS)
+        c.info.n_sdma_xgmi = (int32_t)n;
+    uint32_t status_mask = 0;
+    if (hsa_amd_memory_copy_engine_status(c.agent, c.agent, &status_mask) != HSA_STATUS_SUCCESS)
+        status_mask = 0;
+    c.info.sdma_status_mask = status_mask;
+    uint32_t pref = 0;
+    if (hsa_amd_memory_get_preferred_copy_engine(c.agent, c.agent, &pref) != HSA_STATUS_SUCCESS)
+        pref = 0;
+    c.info.sdma_preferred_mask = pref;
+    profiling_on = hsa_amd_profiling_async_copy_enable(true) == HSA_STATUS_SUCCESS;
+
+    // Candidates: what the status call reports for a device-local copy, else one engine id per
+    // SDMA engine the agent counts (ids are one-hot bits), unless the environment overrides.
+    uint32_t cand = status_mask;
+    if (!cand) {
+        const int total = std::min(16, c.info.n_sdma + c.info.n_sdma_xgmi);
+        for (int b = 0; b < total; ++b) cand |= 1u << b;
+    }
+    if (const char* env = std::getenv("C3_SDMA_ENGINE_MASK"))
+        if (*env) cand = (uint32_t)std::strtoul(env, nullptr, 0);
+    c.sdma_engines.clear();
+    c.info.sdma_engine_mask = 0;
+    if (!cand) return C3_OK;
+
+    // Probe each candidate with one byte-checked device-to-device copy.
+    constexpr size_t kProbe = 256 * 1024;
+    void* src = nullptr;
+    void* dst = nullptr;
+    C3_HIP_TRY(hipMalloc(&src, kProbe));
+    c3_status st = C3_OK;
+    std::vector<uint8_t> want(kProbe), got(kProbe);
+    for (size_t i = 0; i < kProbe; ++i) want[i] = (uint8_t)((i * 131u + 7u) ^ (i >> 9));
+    if (hipMalloc(&dst, kProbe) != hipSuccess ||
+        hipMemcpy(src, want.data(), kProbe, hipMemcpyHostToDevice) != hipSuccess) {
+        st = fail(C3_E_HIP, "SDMA probe: buffer set-up failed");
+    }
+    hsa_signal_t sig{};
+    if (st == C3_OK && hsa_signal_create(1, 0, nullptr, &sig) != HSA_STATUS_SUCCESS)
+        st = fail(C3_E_HSA, "SDMA probe: hsa_signal_create failed");
+    for (int b = 0; st == C3_OK && b < 16; ++b) {
+        const uint32_t engine = 1u << b;
+        if (!(cand & engine)) continue;
+        if (hipMemset(dst, 0, kProbe) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+            st = fail(C3_E_HIP, "SDMA probe: clearing the destination failed");
+            break;
+        }
+        hsa_signal_store_screlease(sig, 1);
+        if (hsa_amd_memory_async_copy_on_engine(dst, c.agent, src, c.agent, kProbe, 0, nullptr, sig,
+                                                (hsa_amd_sdma_engine_id_t)engine,
+                                                true) != HSA_STATUS_SUCCESS)
+            continue;
+        const int64_t deadline = now_ns() + 2000000000ll;
+        hsa_signal_value_t v = hsa_signal_load_scacquire(sig);
+        while (v >= 1 && now_ns() < deadline)
+            v = hsa_signal_wait_scacquire(sig, HSA_SIGNAL_CONDITION_LT, 1,
+                                          system_tick_hz() / 100, HSA_WAIT_STATE_ACTIVE);
+        if (v >= 1) {
+            // The engine never finished: it may still write dst and decrement the signal, so
+            // neither is released (both are leaked on purpose) and initialisation fails.
+            return fail(C3_E_TIMEOUT, "SDMA probe: engine 0x%x did not complete", engine);
+        }
+        if (v != 0) continue;
+        if (hipMemcpy(got.data(), dst, kProbe, hipMemcpyDeviceToHost) != hipSuccess) {
+            st = fail(C3_E_HIP, "SDMA probe: read-back failed");
+            break;
+        }
+        if (std::memcmp(got.data(), want.data(), kProbe) == 0) {
+            c.sdma_engines.push_back(engine);
+            c.info.sdma_engine_mask |= engine;
+        }
+    }
+    if (sig.handle) hsa_signal_destroy(sig);
+    if (dst) (void)hipFree(dst);
+    (void)hipFree(src);
+    return st;
+}
+
+void sdma_release() {
+    for (hsa_signal_t s : signal_pool()) hsa_signal_destroy(s);
+    signal_pool().clear();
+    if (profiling_on) hsa_amd_profiling_async_copy_enable(false);
+    profiling_on = false;
+}
+
+c3_status sdma_issue(const std::vector<Segment>& segs, const c3_move_opts& o, SdmaOp* op) {
+    Context& c = ctx();
+    std::vector<uint32_t> engines;
+    for (uint32_t e : c.sdma_engines)
+        if (o.engine_mask == 0 || (o.engine_mask & e)) engines.push_back(e);
+    if (engines.empty())
+        return fail(C3_E_NO_SDMA,
+                    "no SDMA engine for device-local copies (available mask 0x%x, requested 0x%x)",
+                    c.info.sdma_engine_mask, o.engine_mask);
+
+    struct Chunk {
+        const char* src;
+        char* dst;
+        uint64_t bytes;
+    };
+    std::vector<Chunk> chunks;
+    for (const Segment& s : segs) {
+        if (s.bytes == 0) continue;
+        const uint64_t step = o.chunk_bytes ? o.chunk_bytes : s.bytes;
+        for (uint64_t off = 0; off < s.bytes; off += step)
+            chunks.push_back({static_cast<const char*>(s.src) + off, static_cast<char*>(s.dst) + off,
+                              std::min(step, s.bytes - off)});
+    }
+    const int timeout_ms = o.timeout_ms > 0 ? o.timeout_ms : 20000;
+
+    *op = SdmaOp{};
+    op->fault_mode = o.fault_mode;
+    op->fault_chunk = o.fault_chunk;
+    op->deadline_ns = now_ns() + (int64_t)timeout_ms * 1000000ll;
+    op->signals.reserve(chunks.size());
+    for (size_t i = 0; i < chunks.size(); ++i) {
+        hsa_signal_t sig;
+        c3_status st = get_signal(&sig);
+        if (st != C3_OK) {
+            c3_timing ignore{};
+            (void)sdma_finish(op, &ignore);
+            return st;
+        }
+        const uint32_t engine = engines[i % engines.size()];
+        op->signals.push_back(sig);
+        op->engine_of.push_back(engine);
+        const bool faulted = o.fault_mode != C3_FAULT_NONE && (int)i == o.fault_chunk;
+        if (faulted) {
+            const hsa_signal_value_t v = o.fault_mode == C3_FAULT_DROP_CHUNK  ? 0
+                                         : o.fault_mode == C3_FAULT_ERROR_CHUNK ? -1
+                                                                                : 1;
+            hsa_signal_store_screlease(sig, v);
+            op->issued.push_back(0);
+            continue;
+        }
+        hsa_signal_store_screlease(sig, 1);
+        const hsa_status_t hs = hsa_amd_memory_async_copy_on_engine(
+            chunks[i].dst, c.agent, chunks[i].src, c.agent, chunks[i].bytes, 0, nullptr, sig,
+            (hsa_amd_sdma_engine_id_t)engine, true);
+        if (hs != HSA_STATUS_SUCCESS) {
+            // nothing was queued for this chunk: mark it complete and drain the others
+            hsa_signal_store_screlease(sig, 0);
+            op->issued.push_back(0);
+            const char* m = nullptr;
+            hsa_status_string(hs, &m);
+            c3_timing ignore{};
+            (void)sdma_finish(op, &ignore);
+            return fail(C3_E_HSA, "hsa_amd_memory_async_copy_on_engine(chunk %zu, engine 0x%x, %llu B): %s",
+                        i, engine, (unsigned long long)chunks[i].bytes, m ? m : "?");
+        }
+        op->issued.push_back(1);
+        op->engines_used |= engine;
+    }
+    return C3_OK;
+}
+
+bool sdma_done(const SdmaOp& op) {
+    for (hsa_signal_t s : op.signals)
+        if (hsa_signal_load_scacquire(s) >= 1) return false;
+    return true;
+}
+
+c3_status sdma_finish(SdmaOp* op, c3_timing* t) {
+    const size_t n = op->signals.size();
+    bool hung = false;           // a really issued chunk did not finish in time
+    bool stuck = false;          // a hook-held chunk never finished (expected for STUCK)
+    int errored = -1;
+    // really issued chunks first, so none is in flight when we give up on a held one
+    for (int pass = 0; pass < 2; ++pass) {
+        for (size_t i = 0; i < n; ++i) {
+            if ((pass == 0) != (op->issued[i] == 1)) continue;
+            hsa_signal_t s = op->signals[i];
+            hsa_signal_value_t v = hsa_signal_load_scacquire(s);
+            while (v >= 1) {
+                const int64_t left = op->deadline_ns - now_ns();
+                if (left <= 0) break;
+                const uint64_t hint_ns = (uint64_t)std::min<int64_t>(left, 2000000);
+                const uint64_t hint_ticks = hint_ns * system_tick_hz() / 1000000000ull;
+                v = hsa_signal_wait_scacquire(s, HSA_SIGNAL_CONDITION_LT, 1, hint_ticks,
+                                              HSA_WAIT_STATE_ACTIVE);
+            }
+            if (v >= 1) {
+                if (op->issued[i]) hung = true;
+                else stuck = true;
+            } else if (v < 0 && errored < 0) {
+                errored = (int)i;
+            }
+        }
+    }
+
+    // engine timestamps of the real chunks
+    if (t) {
+        t->n_chunks = (int32_t)n;
+        t->engines_used = op->engines_used;
+        if (profiling_on && !hung) {
+            uint64_t first = UINT64_MAX, last = 0;
+            for (size_t i = 0; i < n; ++i) {
+                if (!op->issued[i]) continue;
+                hsa_amd_profiling_async_copy_time_t ct{};
+                if (hsa_amd_profiling_get_async_copy_time(op->signals[i], &ct) == HSA_STATUS_SUCCESS &&
+                    ct.end >= ct.start && ct.start) {
+                    first = std::min(first, ct.start);
+                    last = std::max(last, ct.end);
+                }
+            }
+            if (last > 0 && first != UINT64_MAX) {
+                const double ns = (double)(last - first) * 1e9 / (double)system_tick_hz();
+                t->copy_gpu_ms = ns * 1e-6;
+                t->sdma_first_start_ns = 0;
+                t->sdma_last_end_ns = (int64_t)ns;
+            }
+        }
+    }
+
+    // return signals: never recycle one an engine may still decrement
+    for (size_t i = 0; i < n; ++i) {
+        const hsa_signal_value_t v = hsa_signal_load_scacquire(op->signals[i]);
+        if (v < 1 || !op->issued[i]) put_signal(op->signals[i]);
+    }
+    op->signals.clear();
+
+    if (hung) return fail(C3_E_TIMEOUT, "SDMA copy did not complete before the deadline");
+    if (errored >= 0)
+        return fail(C3_E_HSA, "SDMA copy of chunk %d reported an error (negative completion signal)",
+                    errored);
+    if (stuck) return fail(C3_E_TIMEOUT, "SDMA chunk held by the test hook never completed");
+    return C3_OK;
+}
+
+}  // namespace c3

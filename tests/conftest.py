@@ -19,3 +19,26 @@ def orc():
 
     oracle.lib()
     return oracle
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name every GPU case on stdout (flushed) before it touches the device."""
+    if request.node.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu-case] {request.node.nodeid}", flush=True)
+    yield
+
+
+@pytest.fixture(scope="session")
+def c3gpu():
+    """libc3 bound to cuda:0. GPU tests fail (never skip) when no GPU is visible."""
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+    from concurrent_gemm_dma_amd import _c3
+
+    _c3.c3_init(0)
+    yield _c3
+    torch.cuda.synchronize()
+    _c3.c3_finalize()

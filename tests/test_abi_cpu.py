@@ -1,0 +1,86 @@
+"""Host-only checks of the C-ABI library: it loads, exports every symbol include/c3.h declares,
+shares torch's single HIP/ROCr runtime, rejects calls before c3_init, and its host-side metric
+arithmetic agrees with the oracle's independent formulas. No GPU work is issued here."""
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "c3.h")
+
+
+@pytest.fixture(scope="module")
+def c3():
+    from concurrent_gemm_dma_amd import _c3
+
+    if not os.path.exists(_c3.LIB_PATH):
+        from concurrent_gemm_dma_amd.build import build
+
+        build()
+    _c3.load()
+    return _c3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:c3_status|const char\*)\s+(c3_\w+)\s*\(", text, re.M)))
+
+
+def test_header_and_binding_agree(c3):
+    assert declared_functions() == sorted(c3.EXPORTS)
+
+
+def test_exports_every_declared_symbol(c3):
+    L = c3.load()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_one_hip_and_one_rocr_runtime(c3):
+    maps = open("/proc/self/maps").read()
+    hip = set(re.findall(r"(\S*/libamdhip64\.so\S*)", maps))
+    hsa = set(re.findall(r"(\S*/libhsa-runtime64\.so\S*)", maps))
+    assert len(hip) == 1 and len(hsa) == 1, (hip, hsa)
+
+
+def test_calls_before_init_are_rejected(c3):
+    # require_init fails before any HIP call is made
+    assert c3.call("c3_gemm", None, None, None, 1, 8, 8, None) == c3.C3_E_NOT_INIT
+    assert "c3_init" in c3.c3_last_error()
+    info = c3.c3_info()
+    assert c3.call("c3_device_info", info) == c3.C3_E_NOT_INIT
+
+
+def test_struct_sizes_match_header_layout(c3):
+    import ctypes
+
+    assert ctypes.sizeof(c3.c3_move_opts) == 40
+    assert ctypes.sizeof(c3.c3_gemm_args) == 48
+    assert ctypes.sizeof(c3.c3_copy_args) == 56 + 40
+    assert ctypes.sizeof(c3.c3_conc_opts) == 32 + 32 + 8 + 8
+    assert ctypes.sizeof(c3.c3_timing) == 8 * 8 + 16
+    assert ctypes.sizeof(c3.c3_metrics) == 6 * 8 + 8
+    assert ctypes.sizeof(c3.c3_info) == 12 * 4 + 8 + 64
+
+
+def test_metrics_agree_with_oracle(c3):
+    from oracle import metrics as om
+
+    rng = np.random.Generator(np.random.PCG64(21))
+    for _ in range(200):
+        tg, tc = rng.uniform(0.1, 10.0, size=2)
+        tconc = rng.uniform(max(tg, tc) * 0.9, (tg + tc) * 1.1)
+        nbytes = rng.uniform(0, 1e12)
+        bw = 8e12
+        got = c3.c3_derive_metrics(tg, tc, tconc, nbytes, bw)
+        want = om.all_metrics(tg, tc, tconc, bytes_total=nbytes, bw_bytes_per_s=bw)
+        for k in ("ideal_speedup", "speedup", "uplift_fraction", "ratio_of_ideal", "gemm_slowdown",
+                  "hbm_ceiling"):
+            assert got[k] == pytest.approx(want[k], rel=1e-12), k
+        assert got["taxonomy"] == want["taxonomy"]
+    assert math.isnan(c3.c3_derive_metrics(1.0, 0.0, 1.0)["uplift_fraction"])
+    with pytest.raises(c3.C3Error):
+        c3.c3_derive_metrics(0.0, 0.0, 1.0)

@@ -1,0 +1,81 @@
+"""Parity at the five workloads' full sizes, in the launch configuration the benchmark times
+(c3_run_concurrent, both movers): the whole copy destination byte-exact, the GEMM checked on
+sampled outputs (random elements, corners, a full row and a full column) against the oracle,
+and bit-exact at full shape with small-integer operands (where the result is unique)."""
+import numpy as np
+import pytest
+
+import oracle
+from concurrent_gemm_dma_amd import workloads as wl
+from gpu_util import bf16_from_dev, bytes_from_dev, empty_bf16, empty_bytes, to_dev
+
+pytestmark = pytest.mark.gpu
+MiB = 1 << 20
+
+
+def sync():
+    import torch
+
+    torch.cuda.synchronize()
+
+
+def run_workload(c3, w, int_exact=False, movers=("sdma", "cu"), n_samples=1024):
+    A, B = wl.gen_gemm_operands(w, int_exact=int_exact)
+    dA, dB = to_dev(A), to_dev(B)
+    dC = empty_bf16((w.M, w.N))
+    if w.copy == "gather":
+        src_np = wl.gen_shards(w)
+        src = [to_dev(s) for s in src_np]
+        want = oracle.gather(src_np)
+    else:
+        src_np = wl.gen_a2a_source(w)
+        src = to_dev(src_np)
+        want = oracle.all2all_block(src_np, w.units, w.unit_bytes)
+    del src_np
+    dst = empty_bytes(want.size)
+    rows, cols = wl.sample_indices(w.M, w.N, n_samples, seed=w.wid, full_rows=(w.M // 3,),
+                                   full_cols=(w.N - 1,))
+    c32, c64, _ = oracle.gemm_elems(A, B, rows, cols)
+    first_c = None
+    for r, mover in enumerate(movers):
+        dC.fill_(-1 - r)
+        dst.fill_(0x5A + r)
+        sync()
+        m = c3.C3_MOVER_SDMA if mover == "sdma" else c3.C3_MOVER_CU
+        if w.copy == "gather":
+            cargs, _keep = c3.gather_args(dst, src, w.unit_bytes, m)
+        else:
+            cargs, _keep = c3.all2all_args(dst, src, w.units, w.unit_bytes, m)
+        t = c3.c3_run_concurrent(c3.gemm_args(dA, dB, dC, w.M, w.N, w.K), cargs,
+                                 c3.conc_opts(comm_first=True))
+        print(f"workload {w.wid} ({w.name}) mover={mover} int_exact={int_exact}: "
+              f"t_conc={t['t_conc_ns'] / 1e6:.3f} ms", flush=True)
+        assert oracle.first_diff(want, bytes_from_dev(dst)) == -1, f"copy mismatch ({mover})"
+        got = bf16_from_dev(dC)
+        sampled = got[rows, cols]
+        if int_exact:
+            np.testing.assert_array_equal(sampled, c32)
+        else:
+            for ref in (c64, c32):
+                rep = oracle.gemm_compare(ref, sampled)
+                assert oracle.gemm_within_tolerance(rep), rep
+        if first_c is None:
+            first_c = got
+        else:
+            np.testing.assert_array_equal(got, first_c)
+    return first_c
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4])
+def test_full_workload(c3gpu, wid):
+    run_workload(c3gpu, wl.WORKLOADS[wid])
+
+
+@pytest.mark.parametrize("total_mib", [32, 1024])
+def test_full_gc_equal_sweep_ends(c3gpu, total_mib):
+    run_workload(c3gpu, wl.WORKLOADS[5].with_gather_total(total_mib * MiB), movers=("sdma",))
+
+
+@pytest.mark.parametrize("wid", [2, 3])
+def test_full_integer_exact(c3gpu, wid):
+    run_workload(c3gpu, wl.WORKLOADS[wid], int_exact=True, movers=("sdma",), n_samples=2048)

@@ -1,0 +1,126 @@
+"""GPU parity of c3_gemm (bf16 MFMA kernels) against the CPU oracle, through the C ABI.
+
+Bar: elementwise |got - ref| <= 1e-2 * max(1, |ref|) and relative Frobenius error <= 1e-3 against
+both the fp64-accumulate definition and the fp32-accumulate triple loop; bit-exact where every
+partial sum is an exact integer (entries in {-2..2}); bit-exact identity; exact zero;
+deterministic (same bits on every run and under any CU mask)."""
+import numpy as np
+import pytest
+
+import oracle
+from concurrent_gemm_dma_amd import workloads as wl
+from gpu_util import bf16_from_dev, empty_bf16, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# (M, N, K): several 256x256x64 tiles with ragged tails, skinny shapes (M <= 64) with ragged N
+# and K, and single-element edges.
+SHAPES = [
+    (1, 8, 8), (3, 24, 40), (16, 264, 136), (17, 520, 328), (33, 1000, 64), (64, 256, 512),
+    (64, 8, 2048), (65, 256, 64), (300, 264, 72), (256, 256, 64), (512, 512, 512),
+    (600, 520, 328), (1024, 776, 1040), (257, 257 + 7, 8),
+]
+
+
+def run_gemm(c3, A, B, stream=None):
+    M, K = A.shape
+    N = B.shape[1]
+    dA, dB = to_dev(A), to_dev(B)
+    dC = empty_bf16((M, N))
+    c3.c3_gemm(dA, dB, dC, M, N, K, stream)
+    import torch
+
+    torch.cuda.synchronize()
+    return bf16_from_dev(dC)
+
+
+def check_tol(ref, got):
+    rep = oracle.gemm_compare(ref, got)
+    assert oracle.gemm_within_tolerance(rep), rep
+    return rep
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_random_normal(c3gpu, M, N, K):
+    A = wl.gen_bf16((M, K), ("normal", 0.0, 1.0), 7000 + M)
+    B = wl.gen_bf16((K, N), ("normal", 0.0, 0.02), 7100 + N + K)
+    got = run_gemm(c3gpu, A, B)
+    check_tol(oracle.gemm_f64acc(A, B), got)
+    check_tol(oracle.gemm_f32acc(A, B), got)
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 512), (17, 520, 328), (600, 520, 328)])
+def test_gemm_uniform(c3gpu, M, N, K):
+    A = wl.gen_bf16((M, K), ("uniform", -1.0, 1.0), 7200 + M)
+    B = wl.gen_bf16((K, N), ("uniform", -1.0, 1.0), 7300 + N)
+    check_tol(oracle.gemm_f64acc(A, B), run_gemm(c3gpu, A, B))
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 520, 4096), (300, 264, 2048), (600, 520, 328), (64, 1024, 8192)])
+def test_gemm_integer_exact(c3gpu, M, N, K):
+    A = wl.gen_small_int_bf16((M, K), 7400 + K)
+    B = wl.gen_small_int_bf16((K, N), 7500 + N)
+    got = run_gemm(c3gpu, A, B)
+    np.testing.assert_array_equal(got, oracle.gemm_f32acc(A, B))
+
+
+@pytest.mark.parametrize("M,K", [(300, 264), (40, 520)])
+def test_gemm_identity(c3gpu, M, K):
+    A = wl.gen_bf16((M, K), ("normal", 0.0, 1.0), 7600 + M)
+    eye = np.where(np.eye(K, dtype=bool), np.uint16(0x3F80), np.uint16(0)).astype(np.uint16)
+    np.testing.assert_array_equal(run_gemm(c3gpu, A, eye), A)
+    B = wl.gen_bf16((M, K), ("normal", 0.0, 1.0), 7700 + K)
+    eyeM = np.where(np.eye(M, dtype=bool), np.uint16(0x3F80), np.uint16(0)).astype(np.uint16)
+    if M % 8 == 0:
+        np.testing.assert_array_equal(run_gemm(c3gpu, eyeM, B), B)
+
+
+def test_gemm_zero(c3gpu):
+    A = np.zeros((300, 136), dtype=np.uint16)
+    B = wl.gen_bf16((136, 264), ("normal", 0.0, 1.0), 7800)
+    got = run_gemm(c3gpu, A, B)
+    assert np.all(oracle.bf16_to_f32(got) == 0.0)
+
+
+def test_gemm_deterministic_and_mask_invariant(c3gpu):
+    import torch
+
+    M, N, K = 1024, 776, 1040
+    A = wl.gen_bf16((M, K), ("normal", 0.0, 1.0), 7900)
+    B = wl.gen_bf16((K, N), ("normal", 0.0, 0.02), 7901)
+    first = run_gemm(c3gpu, A, B)
+    np.testing.assert_array_equal(first, run_gemm(c3gpu, A, B))
+    for keep in (28, 24, 1):
+        mask = c3gpu.c3_cu_mask_balanced(keep)
+        s = c3gpu.c3_stream_create(mask)
+        try:
+            np.testing.assert_array_equal(first, run_gemm(c3gpu, A, B, stream=s))
+        finally:
+            torch.cuda.synchronize()
+            c3gpu.c3_stream_destroy(s)
+    # skinny path too
+    A2 = wl.gen_bf16((16, 8192), ("normal", 0.0, 1.0), 7902)
+    B2 = wl.gen_bf16((8192, 1032), ("normal", 0.0, 0.02), 7903)
+    np.testing.assert_array_equal(run_gemm(c3gpu, A2, B2), run_gemm(c3gpu, A2, B2))
+
+
+def test_gemm_argument_errors(c3gpu):
+    import torch
+
+    dA = torch.zeros((64, 64), dtype=torch.int16, device="cuda:0")
+    dB = torch.zeros((64, 64), dtype=torch.int16, device="cuda:0")
+    dC = torch.zeros((64, 64), dtype=torch.int16, device="cuda:0")
+    call = c3gpu.call
+    ptr = lambda t: t.data_ptr()
+    assert call("c3_gemm", ptr(dA), ptr(dB), ptr(dC), 64, 64, 60, None) == c3gpu.C3_E_INVALID  # K%8
+    assert call("c3_gemm", ptr(dA), ptr(dB), ptr(dC), 64, 60, 64, None) == c3gpu.C3_E_INVALID  # N%8
+    assert call("c3_gemm", ptr(dA) + 2, ptr(dB), ptr(dC), 64, 64, 64, None) == c3gpu.C3_E_INVALID
+    assert call("c3_gemm", None, ptr(dB), ptr(dC), 64, 64, 64, None) == c3gpu.C3_E_INVALID
+    assert call("c3_gemm", ptr(dA), ptr(dB), ptr(dC), 0, 64, 64, None) == c3gpu.C3_E_INVALID
+    assert call("c3_gemm", ptr(dA), ptr(dB), ptr(dA), 64, 64, 64, None) == c3gpu.C3_E_OVERLAP
+    host = np.zeros(64 * 64, dtype=np.uint16)
+    assert call("c3_gemm", host.ctypes.data, ptr(dB), ptr(dC), 64, 64, 64,
+                None) == c3gpu.C3_E_INVALID
+    assert call("c3_gemm", ptr(dA) + (1 << 40), ptr(dB), ptr(dC), 64, 64, 64,
+                None) == c3gpu.C3_E_INVALID
+    torch.cuda.synchronize()
