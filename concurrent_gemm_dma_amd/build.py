@@ -56,8 +56,10 @@ def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def build(verbose: bool = False, save_temps: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, save_temps: bool = False, defines=(), out: str = LIB,
+          build_dir: str = BUILD) -> str:
+    """Compile every source and link `out`. `defines` are extra -D flags for the HIP sources."""
+    os.makedirs(build_dir, exist_ok=True)
     hipcc = os.path.join(ROCM, "bin", "hipcc")
     clangxx = os.path.join(ROCM, "llvm", "bin", "clang++")
     inc = [f"-I{INCLUDE}", f"-I{CSRC}", f"-I{ROCM}/include"]
@@ -65,10 +67,10 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     objs = []
     for src in sources():
         path = os.path.join(CSRC, src)
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(build_dir, src + ".o")
         objs.append(obj)
         if src.endswith(".hip"):
-            cmd = [hipcc] + HIP_FLAGS + inc + ["-c", path, "-o", obj]
+            cmd = [hipcc] + HIP_FLAGS + [f"-D{d}" for d in defines] + inc + ["-c", path, "-o", obj]
             if save_temps:
                 cmd += ["-save-temps=obj"]
         else:
@@ -77,14 +79,14 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tlib = torch_lib_dir()
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     link = [clangxx, "-shared", "-o", tmp] + objs + [
         f"-L{tlib}", "-l:libamdhip64.so", "-l:libhsa-runtime64.so", f"-Wl,-rpath,{tlib}",
         "-Wl,--no-undefined", "-lpthread",
     ]
     _run(link, verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -23,6 +23,7 @@
 #include <algorithm>
 #include <cstdlib>
 #include <map>
+#include <type_traits>
 
 namespace {
 
@@ -194,46 +195,98 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256(
 
     u32x4_t ra[A_LD], rb[B_LD];
 
-    auto load_stage = [&](int k0) {
+    auto load_regs = [&](int k0, u32x4_t* xa, u32x4_t* xb) {
         const bool a_kvalid = (k0 + a_kc * 8) < K;
 #pragma unroll
         for (int i = 0; i < A_LD; ++i)
-            ra[i] = load16(rA, a_kvalid ? a_g0 + (uint32_t)i * a_gstep + (uint32_t)k0 * 2u : kOOB);
+            xa[i] = load16(rA, a_kvalid ? a_g0 + (uint32_t)i * a_gstep + (uint32_t)k0 * 2u : kOOB);
         const __amdgpu_buffer_rsrc_t rB =
             make_rsrc(B + (size_t)k0 * N + n0, ((int64_t)(K - k0) * N - n0) * 2);
 #pragma unroll
         for (int i = 0; i < B_LD; ++i)
-            rb[i] = load16(rB, b_nvalid ? b_g0 + (uint32_t)i * b_gstep : kOOB);
+            xb[i] = load16(rB, b_nvalid ? b_g0 + (uint32_t)i * b_gstep : kOOB);
     };
-    auto store_stage = [&](int s) {
+    auto store_regs = [&](int s, const u32x4_t* xa, const u32x4_t* xb) {
         char* As = smem + s * STAGE;
         char* Bs = As + A_STAGE;
 #pragma unroll
-        for (int i = 0; i < A_LD; ++i) lds_store16(As, a_s0 + (uint32_t)i * 4096u, ra[i]);
+        for (int i = 0; i < A_LD; ++i) lds_store16(As, a_s0 + (uint32_t)i * 4096u, xa[i]);
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i) lds_store16(Bs, b_s0 + (uint32_t)i * 4096u, rb[i]);
+        for (int i = 0; i < B_LD; ++i) lds_store16(Bs, b_s0 + (uint32_t)i * 4096u, xb[i]);
+    };
+    auto load_stage = [&](int k0) { load_regs(k0, ra, rb); };
+    auto store_stage = [&](int s) { store_regs(s, ra, rb); };
+#ifndef C3_GEMM_PIPE
+#define C3_GEMM_PIPE 1
+#endif
+    auto load_frags = [&](const char* As, const char* Bs, int kk, bf16x8_t* colop,
+                          bf16x8_t* rowop) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) colop[mi] = lds_load16(As, a_rd[kk] + mi * 4096u);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+            rowop[ni] = lds_load_tr8(Bs, b_rd[ni] + kk * 8192u, b_rd[ni] + kk * 8192u + 2048u);
+    };
+    auto mfma_block = [&](const bf16x8_t* colop, const bf16x8_t* rowop) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowop[ni], colop[mi],
+                                                                      acc[mi][ni], 0, 0, 0);
     };
     auto compute_stage = [&](int s) {
         const char* As = smem + s * STAGE;
         const char* Bs = As + A_STAGE;
+#if C3_GEMM_PIPE
+        // Operand fragments double-buffered in registers: the 12 LDS reads of step kk+1 are
+        // issued before the 16 MFMAs of step kk (scheduling barriers keep that order), so the
+        // reads complete under the MFMAs instead of stalling them.
+        bf16x8_t colop[2][4], rowop[2][4];
+        load_frags(As, Bs, 0, colop[0], rowop[0]);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk < 3) load_frags(As, Bs, kk + 1, colop[(kk + 1) & 1], rowop[(kk + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_block(colop[kk & 1], rowop[kk & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#else
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             bf16x8_t colop[4], rowop[4];
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi) colop[mi] = lds_load16(As, a_rd[kk] + mi * 4096u);
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                rowop[ni] = lds_load_tr8(Bs, b_rd[ni] + kk * 8192u, b_rd[ni] + kk * 8192u + 2048u);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowop[ni], colop[mi],
-                                                                          acc[mi][ni], 0, 0, 0);
+            load_frags(As, Bs, kk, colop, rowop);
+            mfma_block(colop, rowop);
         }
+#endif
     };
 
     const int nk = (K + BK - 1) / BK;
+#ifndef C3_GEMM_PREFETCH2
+#define C3_GEMM_PREFETCH2 0
+#endif
+#if C3_GEMM_PREFETCH2
+    // Global loads run two K steps ahead in two register sets (the loop is unrolled by two so
+    // each set is named statically): the loads of step k+2 are issued before step k is
+    // computed and written to LDS only at the end of step k+1, giving them two steps of MFMA
+    // work to arrive. LDS stays double-buffered with one barrier per step.
+    u32x4_t ra1[A_LD], rb1[B_LD];
+    load_regs(0, ra, rb);
+    if (nk > 1) load_regs(BK, ra1, rb1);
+    store_regs(0, ra, rb);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+        if (kt + 2 < nk) load_regs((kt + 2) * BK, ra, rb);
+        compute_stage(0);
+        if (kt + 1 < nk) store_regs(1, ra1, rb1);
+        __syncthreads();
+        if (kt + 1 >= nk) break;
+        if (kt + 3 < nk) load_regs((kt + 3) * BK, ra1, rb1);
+        compute_stage(1);
+        if (kt + 2 < nk) store_regs(0, ra, rb);
+        __syncthreads();
+    }
+#else
     load_stage(0);
     store_stage(0);
     __syncthreads();
@@ -244,8 +297,303 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256(
         if (kt + 1 < nk) store_stage(cur ^ 1);
         __syncthreads();
     }
+#endif
 
     // ---- epilogue: lane holds C[m][n..n+3], m = mi*32 + lane%32, n = ni*32 + 8g + 4*(lane/32)
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(C + (size_t)m0 * N + n0, ((int64_t)(M - m0) * N - n0) * 2);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int ml = wm * 128 + mi * 32 + (lane & 31);
+        const bool mvalid = (m0 + ml) < M;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nl = wn * 128 + ni * 32 + 8 * g + 4 * (lane >> 5);
+                const bool ok = mvalid && (n0 + nl) < N;
+                const uint32_t off = ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 2u : kOOB;
+                const f32x16_t& a = acc[mi][ni];
+                store8(rC, off, pack_bf16x4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]));
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
+// 256 x 256 tile kernel, LDS-direct loads
+// ------------------------------------------------------------------------------------------------
+// Same tile, waves and MFMA layout as above, but operands go global -> LDS directly
+// (buffer_load_dwordx4 ... lds: each wave-instruction fills 1 KiB of LDS, lane t's 16 bytes at
+// byte 16*t), so no registers stage them. K step 32, four LDS stages of 32 KiB: the loads of
+// step k+4 are issued as soon as every wave has finished reading step k, i.e. about three and a
+// half steps of MFMA work before they are needed. Per step: read the second half of this step's
+// fragments, run the first half's MFMAs, wait for step k+1 and barrier, refill this step's
+// buffer, read the first half of step k+1's fragments, run the second half's MFMAs.
+namespace td {
+constexpr int BM = 256, BN = 256, BK = 32, NT = 256, NSTAGE = 4;
+constexpr int A_STAGE = BM * BK * 2;  // 16 KiB: 256 rows of 64 B
+constexpr int B_STAGE = BK * BN * 2;  // 16 KiB: 32 rows of 512 B
+constexpr int STAGE = A_STAGE + B_STAGE;
+#ifndef C3_GEMM_GROUP_M
+#define C3_GEMM_GROUP_M 4
+#endif
+constexpr int GROUP_M = C3_GEMM_GROUP_M;
+constexpr int LOADS_PER_STAGE = 8;    // per wave: 4 A + 4 B wave-instructions
+}  // namespace td
+
+// A rows of 64 B (4 chunks): chunk ^= 2*(r2^r3) + (r1^r2) (r_i = bit i of the row). Distinct
+// within every 8 consecutive rows of one parity and within every 4 rows 4 apart, so 8 or 16
+// lanes reading 16 B from consecutive rows hit distinct banks.
+__device__ __forceinline__ int swz_a32(int row) {
+    const int b1 = (row >> 1) & 1, b2 = (row >> 2) & 1, b3 = (row >> 3) & 1;
+    return ((b2 ^ b3) << 1) | (b1 ^ b2);
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+#define C3_WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 15) | (7 << 4) | (15 << 8) | (((n) >> 4) << 14))
+
+// Raw buffer resource as four dwords (gfx9 layout: base, base_hi | stride << 16, records, word 3).
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t make_rsrc_words(const void* base, int64_t bytes) {
+    uint64_t n = bytes <= 0 ? 0ull : (uint64_t)bytes;
+    if (n > kMaxRecords) n = kMaxRecords;
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    i32x4_t w;
+    w.x = (int)(uint32_t)a;
+    w.y = (int)((uint32_t)(a >> 32) & 0xFFFFu);
+    w.z = (int)(uint32_t)n;
+    w.w = kRsrcWord3;
+    return w;
+}
+
+// One LDS-direct 16-byte load per lane: lane t's 16 bytes from `voff` land at LDS byte address
+// lds_addr + 16*t (lds_addr wave-uniform). Issued through inline asm so that the compiler's wait
+// insertion, which cannot tell these writes from the transpose reads of other LDS stages and
+// would wait for every outstanding load before each read, leaves them alone; the kernel waits
+// on the vector-memory counter itself (C3_WAIT_VMCNT) before it reads a stage. M0 carries the
+// LDS address; nothing else in these kernels uses M0.
+__device__ __forceinline__ void lds_dma16_at(i32x4_t r, uint32_t lds_addr, uint32_t voff) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(lds_addr), "v"(voff), "s"(r)
+        : "memory", "m0");
+}
+
+__device__ __forceinline__ void lds_dma16(i32x4_t r, char* lds, uint32_t voff) {
+    lds_dma16_at(r, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(C3_LDS char*)lds), voff);
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
+    int M, int N, int K, int tiles_m, int tiles_n) {
+    using namespace td;
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int tm, tn;
+    map_tile<GROUP_M>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // ---- global -> LDS addressing. Wave w fills A blocks w*4+j (16 rows each) and B blocks
+    // w*4+j (2 k rows each), j = 0..3; lane t lands at byte 16*t of the 1 KiB block.
+    const i32x4_t rA = make_rsrc_words(A + (size_t)m0 * K, (int64_t)(M - m0) * K * 2);
+    const int a_row0 = 16 * (wave * 4) + (lane >> 2);           // + 16*j
+    const int a_kc = (lane & 3) ^ swz_a32(a_row0);               // same for every j
+    const uint32_t a_g0 = (uint32_t)a_row0 * (uint32_t)K * 2u + (uint32_t)a_kc * 16u;
+    const uint32_t a_gstep = 16u * (uint32_t)K * 2u;
+    uint32_t b_g[4];
+    bool b_ok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int krow = 2 * (wave * 4 + j) + (lane >> 5);
+        const int nc = (lane & 31) ^ swz_b(krow);
+        b_g[j] = (uint32_t)krow * (uint32_t)N * 2u + (uint32_t)nc * 16u;
+        b_ok[j] = (n0 + nc * 8) < N;
+    }
+    auto issue_stage = [&](int k0, int s) {
+        char* As = smem + s * STAGE;
+        char* Bs = As + A_STAGE;
+        const bool a_ok = (k0 + a_kc * 8) < K;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            lds_dma16(rA, As + (wave * 4 + j) * 1024,
+                      a_ok ? a_g0 + (uint32_t)j * a_gstep + (uint32_t)k0 * 2u : kOOB);
+        const i32x4_t rB =
+            make_rsrc_words(B + (size_t)k0 * N + n0, ((int64_t)(K - k0) * N - n0) * 2);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lds_dma16(rB, Bs + (wave * 4 + j) * 1024, b_ok[j] ? b_g[j] : kOOB);
+    };
+
+    // ---- LDS -> MFMA operand addressing ----
+    const int ar = lane & 31;
+    uint32_t a_rd[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+        a_rd[kk] = (uint32_t)(wm * 128 + ar) * 64u +
+                   (uint32_t)((((kk * 2) + (lane >> 5)) ^ swz_a32(ar)) << 4);
+    const int G = lane >> 4, p = lane & 15;
+    const int b_sw = swz_b(p >> 2);
+    uint32_t b_rd[4];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+        const int nc = wn * 16 + ni * 4 + 2 * (G & 1) + ((p >> 1) & 1);
+        b_rd[ni] = (uint32_t)(8 * (G >> 1) + (p >> 2)) * 512u + (uint32_t)((nc ^ b_sw) << 4) +
+                   (uint32_t)((p & 1) * 8);
+    }
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x16_t{};
+
+    auto load_frags = [&](int s, int kk, bf16x8_t* colop, bf16x8_t* rowop) {
+        const char* As = smem + s * STAGE;
+        const char* Bs = As + A_STAGE;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) colop[mi] = lds_load16(As, a_rd[kk] + mi * 2048u);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+            rowop[ni] = lds_load_tr8(Bs, b_rd[ni] + kk * 8192u, b_rd[ni] + kk * 8192u + 2048u);
+    };
+    auto mfma_block = [&](const bf16x8_t* colop, const bf16x8_t* rowop) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowop[ni], colop[mi],
+                                                                      acc[mi][ni], 0, 0, 0);
+    };
+
+    const int nk = (K + BK - 1) / BK;
+#pragma unroll
+    for (int s = 0; s < NSTAGE; ++s)
+        if (s < nk) issue_stage(s * BK, s);
+    if (nk >= 4) C3_WAIT_VMCNT(3 * LOADS_PER_STAGE);
+    else if (nk == 3) C3_WAIT_VMCNT(2 * LOADS_PER_STAGE);
+    else if (nk == 2) C3_WAIT_VMCNT(1 * LOADS_PER_STAGE);
+    else C3_WAIT_VMCNT(0);
+    __syncthreads();
+
+#ifndef C3_GEMM_INTERLEAVE
+#define C3_GEMM_INTERLEAVE 1
+#endif
+#if C3_GEMM_INTERLEAVE
+    // With one wave per SIMD the MFMA pipe idles whenever the wave issues anything else between
+    // two MFMAs, so every other instruction is slotted one-for-one behind an MFMA (scheduling
+    // fences after each slot keep this order): while an MFMA occupies the pipe for its 32
+    // cycles the wave issues the next LDS read or LDS-direct load, and the next MFMA is ready
+    // the moment the pipe frees.
+    bf16x8_t cf[2][4];
+    i16x4_t rlo[2][4], rhi[2][4];
+    auto read_item = [&](int s, int kk, int set, int j) {
+        const char* As = smem + s * STAGE;
+        const char* Bs = As + A_STAGE;
+        if (j < 4) {
+            cf[set][j] = lds_load16(As, a_rd[kk] + j * 2048u);
+        } else {
+            const int ni = (j - 4) >> 1;
+            const uint32_t off = b_rd[ni] + kk * 8192u + ((j - 4) & 1) * 2048u;
+            const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                reinterpret_cast<C3_LDS i16x4_t*>((C3_LDS char*)Bs + off));
+            if ((j - 4) & 1) rhi[set][ni] = v;
+            else rlo[set][ni] = v;
+        }
+    };
+    auto mfma_item = [&](int set, int i) {
+        const int mi = i >> 2, ni = i & 3;
+        const i16x8_t rv = __builtin_shufflevector(rlo[set][ni], rhi[set][ni], 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, rv),
+                                                              cf[set][mi], acc[mi][ni], 0, 0, 0);
+    };
+    // Wave-uniform LDS byte addresses of this wave's LDS-direct destinations in stage 0.
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(C3_LDS char*)smem;
+    const uint32_t wave_u = __builtin_amdgcn_readfirstlane((uint32_t)wave);
+    const uint32_t a_dst0 = lds_base + wave_u * 4096u;
+    const uint32_t b_dst0 = lds_base + (uint32_t)A_STAGE + wave_u * 4096u;
+
+    // One K step. REFILL: issue step kt+4's loads into this step's buffer (steady state);
+    // NEXT: read step kt+1's first fragments. Compile-time flags keep each loop body
+    // straight-line (branches around the MFMA sequence cost the accumulators their registers).
+    auto step = [&](int kt, auto refill_c, auto next_c) {
+        constexpr bool REFILL = decltype(refill_c)::value;
+        constexpr bool NEXT = decltype(next_c)::value;
+        const int s = kt & (NSTAGE - 1);
+        // first half: MFMAs of k-slice 0 (set 0) with the reads of k-slice 1 (set 1)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            mfma_item(0, i);
+            if (i < 12) read_item(s, 1, 1, i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // step kt+1 landed for this wave (steps kt+2, kt+3 may still be in flight); this
+        // wave's reads of step kt are done; then every wave is past both points
+        if (REFILL || kt + 3 < nk) C3_WAIT_VMCNT(2 * LOADS_PER_STAGE);
+        else if (kt + 2 < nk) C3_WAIT_VMCNT(1 * LOADS_PER_STAGE);
+        else C3_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        // second half: MFMAs of k-slice 1 (set 1) with the reads of step kt+1's k-slice 0
+        // (set 0) and the refill of this step's buffer for step kt+4
+        const int s1 = (kt + 1) & (NSTAGE - 1);
+        const int k0 = (kt + NSTAGE) * BK;
+        const bool a_ok = (k0 + a_kc * 8) < K;
+        i32x4_t rB{};
+        if (REFILL) rB = make_rsrc_words(B + (size_t)k0 * N + n0, ((int64_t)(K - k0) * N - n0) * 2);
+        const uint32_t a_dst = a_dst0 + (uint32_t)s * STAGE;
+        const uint32_t b_dst = b_dst0 + (uint32_t)s * STAGE;
+        const uint32_t a_off = a_g0 + (uint32_t)k0 * 2u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            mfma_item(1, i);
+            if (NEXT && i < 12) read_item(s1, 0, 0, i);
+            if (REFILL && i < 4)
+                lds_dma16_at(rA, a_dst + i * 1024u, a_ok ? a_off + (uint32_t)i * a_gstep : kOOB);
+            if (REFILL && i >= 4 && i < 8)
+                lds_dma16_at(rB, b_dst + (i - 4) * 1024u, b_ok[i - 4] ? b_g[i - 4] : kOOB);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+#pragma unroll
+    for (int j = 0; j < 12; ++j) read_item(0, 0, 0, j);
+    int kt = 0;
+    for (; kt + NSTAGE < nk; ++kt) step(kt, std::true_type{}, std::true_type{});
+    for (; kt + 1 < nk; ++kt) step(kt, std::false_type{}, std::true_type{});
+    if (kt < nk) step(kt, std::false_type{}, std::false_type{});
+#else
+    bf16x8_t c0[4], r0[4], c1[4], r1[4];
+    load_frags(0, 0, c0, r0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int s = kt & (NSTAGE - 1);
+        load_frags(s, 1, c1, r1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_block(c0, r0);
+        __builtin_amdgcn_sched_barrier(0);
+        // step kt+1 landed for this wave; stages kt+2, kt+3 may still be in flight
+        if (kt + 3 < nk) C3_WAIT_VMCNT(2 * LOADS_PER_STAGE);
+        else if (kt + 2 < nk) C3_WAIT_VMCNT(1 * LOADS_PER_STAGE);
+        else C3_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of step kt are done
+        __syncthreads();
+        if (kt + NSTAGE < nk) issue_stage((kt + NSTAGE) * BK, s);
+        if (kt + 1 < nk) load_frags((kt + 1) & (NSTAGE - 1), 0, c0, r0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_block(c1, r1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#endif
+
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc(C + (size_t)m0 * N + n0, ((int64_t)(M - m0) * N - n0) * 2);
 #pragma unroll
@@ -507,8 +855,16 @@ c3_status gemm_enqueue(const GemmPlan& p, hipStream_t stream) {
     if (p.kind == 0) {
         const int tiles_m = (p.M + t256::BM - 1) / t256::BM;
         const int tiles_n = (p.N + t256::BN - 1) / t256::BN;
+#ifndef C3_GEMM_KERNEL
+#define C3_GEMM_KERNEL 1
+#endif
+#if C3_GEMM_KERNEL == 1
+        hipLaunchKernelGGL(gemm_bf16_tile256_dma, dim3(tiles_m * tiles_n), dim3(td::NT), 0, stream,
+                           A, B, C, p.M, p.N, p.K, tiles_m, tiles_n);
+#else
         hipLaunchKernelGGL(gemm_bf16_tile256, dim3(tiles_m * tiles_n), dim3(t256::NT), 0, stream,
                            A, B, C, p.M, p.N, p.K, tiles_m, tiles_n);
+#endif
         C3_HIP_TRY(hipGetLastError());
         return C3_OK;
     }
