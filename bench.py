@@ -120,15 +120,17 @@ def main():
         ddst.fill_((0xA5 + poison_i[0]) & 0xFF)
         torch.cuda.synchronize()
 
-    # ---- isolated GEMM: reference bits + time ----
     iso_c = None
-    t_gemm, g_gpu = [], []
-    for i in range(args.warmup + args.steps):
-        poison()
-        t = c3.c3_run_concurrent(gargs, None, c3.conc_opts(gemm_mask=gmask, flush_bytes=FLUSH_BYTES))
-        if i >= args.warmup:
-            t_gemm.append(t["t_conc_ns"] * 1e-9)
-            g_gpu.append(t["gemm_gpu_ms"] * 1e-3)
+
+    def verify_copy(label):
+        if args.profile:
+            return
+        if not torch.equal(ddst, dwant):
+            host = ddst.cpu().numpy()
+            raise SystemExit(f"{label}: copy mismatch at byte {oracle.first_diff(want, host)}")
+
+    def verify_c(label):
+        nonlocal iso_c
         if iso_c is None:
             iso_c = dC.clone()
             if not args.profile:
@@ -136,77 +138,90 @@ def main():
                 rep = oracle.gemm_compare(ref64, got)
                 if not oracle.gemm_within_tolerance(rep):
                     raise SystemExit(f"GEMM parity failure vs oracle: {rep}")
-                log(f"GEMM sampled parity vs oracle ok ({rep['n']} elems, {rep['n_diff']} differ by rounding)")
+                log(f"GEMM sampled parity vs oracle ok ({rep['n']} elems, "
+                    f"{rep['n_diff']} differ by one rounding)")
         elif not args.profile and not torch.equal(dC, iso_c):
-            raise SystemExit("isolated GEMM is not deterministic")
+            raise SystemExit(f"{label}: C differs from the isolated GEMM")
+
+    movers = (("sdma", c3.C3_MOVER_SDMA), ("cu", c3.C3_MOVER_CU))
+    copy_args = {name: cargs(mv) for name, mv in movers}
+    conc = {}
+    for name, mv in movers:
+        cmask = None
+        if gmask is not None and mv == c3.C3_MOVER_CU:
+            cmask = c3.c3_cu_mask_balanced(args.keep_per_xcc, complement=True)
+        conc[name] = c3.conc_opts(gemm_mask=gmask, comm_mask=cmask, comm_first=comm_first,
+                                  flush_bytes=FLUSH_BYTES)
+    iso_g_opts = c3.conc_opts(gemm_mask=gmask, flush_bytes=FLUSH_BYTES)
+    iso_c_opts = c3.conc_opts(flush_bytes=FLUSH_BYTES)
+
+    # Every round runs the isolated GEMM, then per mover the isolated copy and the concurrent
+    # step, so that clock and thermal drift affect isolated and concurrent times alike.
+    t_gemm, g_gpu = [], []
+    rec = {name: {"t_copy": [], "c_gpu": [], "t_conc": [], "gk": []} for name, _ in movers}
+    torch.cuda.synchronize()
+    wall0 = None
+    for i in range(args.warmup + args.steps):
+        if i == args.warmup:
+            torch.cuda.synchronize()
+            wall0 = time.time()
+        timed = i >= args.warmup
+        poison()
+        t = c3.c3_run_concurrent(gargs, None, iso_g_opts)
+        verify_c(f"isolated GEMM {i}")
+        if timed:
+            t_gemm.append(t["t_conc_ns"] * 1e-9)
+            g_gpu.append(t["gemm_gpu_ms"] * 1e-3)
+        for name, mv in movers:
+            ca = copy_args[name][0]
+            r = rec[name]
+            poison()
+            t = c3.c3_run_concurrent(None, ca, iso_c_opts)
+            verify_copy(f"isolated {name} copy {i}")
+            if timed:
+                r["t_copy"].append(t["t_conc_ns"] * 1e-9)
+                r["c_gpu"].append(t["copy_gpu_ms"] * 1e-3)
+            poison()
+            t = c3.c3_run_concurrent(gargs, ca, conc[name])
+            verify_copy(f"{name} step {i}")
+            verify_c(f"{name} step {i}")
+            if timed:
+                r["t_conc"].append(t["t_conc_ns"] * 1e-9)
+                r["gk"].append(t["gemm_gpu_ms"] * 1e-3)
+    torch.cuda.synchronize()
+    wall = time.time() - wall0
     T_gemm = statistics.median(t_gemm)
     log(f"isolated GEMM: median {T_gemm * 1e3:.3f} ms  ({flops / T_gemm / 1e12:.1f} TFLOP/s host, "
         f"{flops / statistics.median(g_gpu) / 1e12:.1f} TFLOP/s events)")
 
-    def verify(label):
-        if args.profile:
-            return
-        if not torch.equal(ddst, dwant):
-            host = ddst.cpu().numpy()
-            raise SystemExit(f"{label}: copy mismatch at byte {oracle.first_diff(want, host)}")
-        if not torch.equal(dC, iso_c):
-            raise SystemExit(f"{label}: C differs from the isolated GEMM")
-
     results = {}
-    for mover_name, mover in (("sdma", c3.C3_MOVER_SDMA), ("cu", c3.C3_MOVER_CU)):
-        ca, _keep = cargs(mover)
-        # isolated copy
-        t_copy, c_gpu = [], []
-        for i in range(args.warmup + args.steps):
-            poison()
-            t = c3.c3_run_concurrent(None, ca, c3.conc_opts(flush_bytes=FLUSH_BYTES))
-            if not args.profile and not torch.equal(ddst, dwant):
-                raise SystemExit(f"isolated {mover_name} copy mismatch")
-            if i >= args.warmup:
-                t_copy.append(t["t_conc_ns"] * 1e-9)
-                c_gpu.append(t["copy_gpu_ms"] * 1e-3)
-        T_copy = statistics.median(t_copy)
-        # concurrent steps (timed region: the library's clock from first issue to both complete)
-        cmask = None
-        if gmask is not None and mover == c3.C3_MOVER_CU:
-            cmask = c3.c3_cu_mask_balanced(args.keep_per_xcc, complement=True)
-        opts = c3.conc_opts(gemm_mask=gmask, comm_mask=cmask, comm_first=comm_first,
-                            flush_bytes=FLUSH_BYTES)
-        t_conc, gk = [], []
-        torch.cuda.synchronize()
-        wall0 = time.time()
-        for i in range(args.warmup + args.steps):
-            poison()
-            t = c3.c3_run_concurrent(gargs, ca, opts)
-            verify(f"{mover_name} step {i}")
-            if i >= args.warmup:
-                t_conc.append(t["t_conc_ns"] * 1e-9)
-                gk.append(t["gemm_gpu_ms"] * 1e-3)
-        torch.cuda.synchronize()
-        wall = time.time() - wall0
-        T_conc = statistics.mean(t_conc)
+    for name, _ in movers:
+        r = rec[name]
+        T_copy = statistics.median(r["t_copy"])
+        T_conc = statistics.mean(r["t_conc"])
+        c_gpu_med = statistics.median(r["c_gpu"])
         m = c3.c3_derive_metrics(T_gemm, T_copy, T_conc, float(w.gemm_bytes + 2 * copy_bytes),
                                  PEAK_HBM_GBPS * 1e9)
-        results[mover_name] = {
+        results[name] = {
             "t_copy_ms": T_copy * 1e3, "t_conc_ms": T_conc * 1e3,
-            "t_conc_ms_min": min(t_conc) * 1e3, "t_conc_ms_max": max(t_conc) * 1e3,
-            "t_conc_ms_std": (statistics.pstdev(t_conc) * 1e3) if len(t_conc) > 1 else 0.0,
+            "t_conc_ms_min": min(r["t_conc"]) * 1e3, "t_conc_ms_max": max(r["t_conc"]) * 1e3,
+            "t_conc_ms_std": (statistics.pstdev(r["t_conc"]) * 1e3) if len(r["t_conc"]) > 1 else 0.0,
             "copy_gbps_isolated": 2 * copy_bytes / T_copy / 1e9,
-            "copy_gbps_isolated_engine_clock": (2 * copy_bytes / statistics.median(c_gpu) / 1e9
-                                                if statistics.median(c_gpu) > 0 else None),
+            "copy_gbps_isolated_engine_clock": (2 * copy_bytes / c_gpu_med / 1e9
+                                                if c_gpu_med > 0 else None),
             "gemm_tflops_concurrent": flops / T_conc / 1e12,
             "copy_gbps_concurrent": 2 * copy_bytes / T_conc / 1e9,
-            "gemm_kernel_ms_concurrent": statistics.mean(gk) * 1e3,
-            "wall_s_with_verification": wall,
+            "gemm_kernel_ms_concurrent": statistics.mean(r["gk"]) * 1e3,
             **{k: m[k] for k in ("ideal_speedup", "speedup", "uplift_fraction", "ratio_of_ideal",
                                  "gemm_slowdown", "hbm_ceiling", "taxonomy")},
         }
-        log(f"{mover_name}: T_copy {T_copy * 1e3:.3f} ms ({results[mover_name]['copy_gbps_isolated']:.0f} GB/s), "
+        log(f"{name}: T_copy {T_copy * 1e3:.3f} ms ({results[name]['copy_gbps_isolated']:.0f} GB/s), "
             f"T_conc {T_conc * 1e3:.3f} ms, S {m['speedup']:.4f} / ideal {m['ideal_speedup']:.4f}, "
             f"uplift {m['uplift_fraction'] * 100:.1f}%")
 
-    # ---- roofline of the dominant kernel (the GEMM), HIP events on its own stream ----
-    gemm_kernel_s = statistics.mean(g_gpu)
+    # ---- roofline of the dominant kernel (the GEMM): HIP events recorded by the library on the
+    # GEMM's own stream around every launch of the timed SDMA-concurrent steps ----
+    gemm_kernel_s = statistics.mean(rec["sdma"]["gk"])
     achieved_tflops = flops / gemm_kernel_s / 1e12
     roofline = {"bound": "mfma" if M > 64 else "hbm",
                 "achieved": None, "peak": None, "unit": None, "frac": None, "traffic": None}
@@ -270,6 +285,10 @@ def main():
         "t_gemm_ms": round(T_gemm * 1e3, 4),
         "movers": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                    for k, v in results.items()},
+        "timing": "ms_per_step = mean over the timed steps of the library's host clock from the "
+                  "first issue to both operations complete (SDMA cell); isolated and concurrent "
+                  "runs interleaved per step, each after a poison + 512 MiB cache flush",
+        "wall_s_timed_rounds": round(wall, 3),
         "verified": "every step: copy byte-exact vs oracle, C bit-identical to isolated C; "
                     "isolated C vs oracle on sampled elements",
         "roofline": roofline,

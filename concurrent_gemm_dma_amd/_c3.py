@@ -120,13 +120,16 @@ class c3_metrics(ctypes.Structure):
 _lib = None
 
 
-def load(path: str = LIB_PATH):
-    """Open libc3.so (after importing torch so both share one HIP runtime)."""
+def load(path: Optional[str] = None):
+    """Open libc3.so (after importing torch so both share one HIP runtime). The path defaults
+    to the in-tree build; the C3_LIB environment variable names another build of it."""
     global _lib
     if _lib is not None:
         return _lib
     import torch  # noqa: F401  (loads the HIP/ROCr runtime libc3 binds to)
 
+    if path is None:
+        path = os.environ.get("C3_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise FileNotFoundError(f"{path} is not built; run __graft_entry__.build() "
                                 "(python -m concurrent_gemm_dma_amd.build)")

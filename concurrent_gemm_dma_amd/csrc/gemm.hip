@@ -475,6 +475,32 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     };
 
     const int nk = (K + BK - 1) / BK;
+#ifndef C3_GEMM_INTERLEAVE
+#define C3_GEMM_INTERLEAVE 1
+#endif
+#ifndef C3_GEMM_DMA_SPLIT
+#define C3_GEMM_DMA_SPLIT 1
+#endif
+#if C3_GEMM_INTERLEAVE && C3_GEMM_DMA_SPLIT
+    // Split refill: a stage's A half is issued one half-step earlier than its B half, so the
+    // prologue issues stages 0..2 whole and only the A half of stage 3.
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s)
+        if (s < nk) issue_stage(s * BK, s);
+    if (nk > NSTAGE - 1) {
+        const int k0 = (NSTAGE - 1) * BK;
+        const bool a_ok = (k0 + a_kc * 8) < K;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            lds_dma16(rA, smem + (NSTAGE - 1) * STAGE + (wave * 4 + j) * 1024,
+                      a_ok ? a_g0 + (uint32_t)j * a_gstep + (uint32_t)k0 * 2u : kOOB);
+    }
+    // loads issued after stage 0's last one: A1 B1 A2 B2 A3 (those that exist)
+    if (nk >= 4) C3_WAIT_VMCNT(5 * 4);
+    else if (nk == 3) C3_WAIT_VMCNT(4 * 4);
+    else if (nk == 2) C3_WAIT_VMCNT(2 * 4);
+    else C3_WAIT_VMCNT(0);
+#else
 #pragma unroll
     for (int s = 0; s < NSTAGE; ++s)
         if (s < nk) issue_stage(s * BK, s);
@@ -482,11 +508,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     else if (nk == 3) C3_WAIT_VMCNT(2 * LOADS_PER_STAGE);
     else if (nk == 2) C3_WAIT_VMCNT(1 * LOADS_PER_STAGE);
     else C3_WAIT_VMCNT(0);
+#endif
     __syncthreads();
 
-#ifndef C3_GEMM_INTERLEAVE
-#define C3_GEMM_INTERLEAVE 1
-#endif
 #if C3_GEMM_INTERLEAVE
     // With one wave per SIMD the MFMA pipe idles whenever the wave issues anything else between
     // two MFMAs, so every other instruction is slotted one-for-one behind an MFMA (scheduling
@@ -521,23 +545,36 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     const uint32_t a_dst0 = lds_base + wave_u * 4096u;
     const uint32_t b_dst0 = lds_base + (uint32_t)A_STAGE + wave_u * 4096u;
 
-    // One K step. REFILL: issue step kt+4's loads into this step's buffer (steady state);
-    // NEXT: read step kt+1's first fragments. Compile-time flags keep each loop body
-    // straight-line (branches around the MFMA sequence cost the accumulators their registers).
-    auto step = [&](int kt, auto refill_c, auto next_c) {
-        constexpr bool REFILL = decltype(refill_c)::value;
-        constexpr bool NEXT = decltype(next_c)::value;
+    // One K step, with compile-time flags (each loop body stays straight-line: branches around
+    // the MFMA sequence cost the accumulators their registers):
+    //   BA - first half issues the B half of step kt+3 into buffer (kt+3)%4 (split refill; that
+    //        buffer's last reader, step kt-1, finished before the previous step's barrier),
+    //   RA - second half issues the A half of step kt+4 into this step's buffer,
+    //   RB - second half issues the B half of step kt+4 too (whole refill),
+    //   NX - second half reads step kt+1's first fragments.
+    auto step = [&](int kt, auto ba_c, auto ra_c, auto rb_c, auto nx_c) {
+        constexpr bool BA = decltype(ba_c)::value;
+        constexpr bool RA = decltype(ra_c)::value;
+        constexpr bool RB = decltype(rb_c)::value;
+        constexpr bool NX = decltype(nx_c)::value;
         const int s = kt & (NSTAGE - 1);
+        const int s3 = (kt + NSTAGE - 1) & (NSTAGE - 1);
+        const int k3 = (kt + NSTAGE - 1) * BK;
+        i32x4_t rB3{};
+        if (BA) rB3 = make_rsrc_words(B + (size_t)k3 * N + n0, ((int64_t)(K - k3) * N - n0) * 2);
+        const uint32_t b_dst3 = b_dst0 + (uint32_t)s3 * STAGE;
         // first half: MFMAs of k-slice 0 (set 0) with the reads of k-slice 1 (set 1)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             mfma_item(0, i);
             if (i < 12) read_item(s, 1, 1, i);
+            if (BA && i >= 4 && i < 8)
+                lds_dma16_at(rB3, b_dst3 + (i - 4) * 1024u, b_ok[i - 4] ? b_g[i - 4] : kOOB);
             __builtin_amdgcn_sched_barrier(0);
         }
         // step kt+1 landed for this wave (steps kt+2, kt+3 may still be in flight); this
         // wave's reads of step kt are done; then every wave is past both points
-        if (REFILL || kt + 3 < nk) C3_WAIT_VMCNT(2 * LOADS_PER_STAGE);
+        if (RA || kt + 3 < nk) C3_WAIT_VMCNT(2 * LOADS_PER_STAGE);
         else if (kt + 2 < nk) C3_WAIT_VMCNT(1 * LOADS_PER_STAGE);
         else C3_WAIT_VMCNT(0);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -549,28 +586,38 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         const int k0 = (kt + NSTAGE) * BK;
         const bool a_ok = (k0 + a_kc * 8) < K;
         i32x4_t rB{};
-        if (REFILL) rB = make_rsrc_words(B + (size_t)k0 * N + n0, ((int64_t)(K - k0) * N - n0) * 2);
+        if (RB) rB = make_rsrc_words(B + (size_t)k0 * N + n0, ((int64_t)(K - k0) * N - n0) * 2);
         const uint32_t a_dst = a_dst0 + (uint32_t)s * STAGE;
         const uint32_t b_dst = b_dst0 + (uint32_t)s * STAGE;
         const uint32_t a_off = a_g0 + (uint32_t)k0 * 2u;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             mfma_item(1, i);
-            if (NEXT && i < 12) read_item(s1, 0, 0, i);
-            if (REFILL && i < 4)
+            if (NX && i < 12) read_item(s1, 0, 0, i);
+            if (RA && i < 4)
                 lds_dma16_at(rA, a_dst + i * 1024u, a_ok ? a_off + (uint32_t)i * a_gstep : kOOB);
-            if (REFILL && i >= 4 && i < 8)
+            if (RB && i >= 4 && i < 8)
                 lds_dma16_at(rB, b_dst + (i - 4) * 1024u, b_ok[i - 4] ? b_g[i - 4] : kOOB);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    using T = std::true_type;
+    using F = std::false_type;
 
 #pragma unroll
     for (int j = 0; j < 12; ++j) read_item(0, 0, 0, j);
     int kt = 0;
-    for (; kt + NSTAGE < nk; ++kt) step(kt, std::true_type{}, std::true_type{});
-    for (; kt + 1 < nk; ++kt) step(kt, std::false_type{}, std::true_type{});
-    if (kt < nk) step(kt, std::false_type{}, std::false_type{});
+#if C3_GEMM_DMA_SPLIT
+    for (; kt + NSTAGE < nk; ++kt) step(kt, T{}, T{}, F{}, T{});
+    if (kt + NSTAGE - 1 < nk) {
+        step(kt, T{}, F{}, F{}, T{});
+        ++kt;
+    }
+#else
+    for (; kt + NSTAGE < nk; ++kt) step(kt, F{}, T{}, T{}, T{});
+#endif
+    for (; kt + 1 < nk; ++kt) step(kt, F{}, F{}, F{}, T{});
+    if (kt < nk) step(kt, F{}, F{}, F{}, F{});
 #else
     bf16x8_t c0[4], r0[4], c1[4], r1[4];
     load_frags(0, 0, c0, r0);
