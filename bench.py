@@ -2,18 +2,27 @@
 """Benchmark of the C3 hot path on one MI355X: a bf16 GEMM concurrent with a collective-shaped
 copy, moved by the SDMA engines (headline) and by a CU kernel (baseline).
 
-A step is one concurrent run (c3_run_concurrent) of the whole path over the workload: GEMM and
-copy issued (communication first), both completed. Before every step, untimed: the outputs are
-poisoned and the Infinity Cache is flushed (inside the library, before its clock starts). After
-every step, untimed: the copy destination is compared byte for byte with the oracle's gather and
-C bit for bit with the GEMM's isolated result (itself checked against the oracle on sampled
-elements). Isolated GEMM and copy times use the same protocol and feed the ideal speedup.
+Default mode (`--mode c3`, the contract): a step is one concurrent run (c3_run_concurrent) of
+the whole path over the workload: GEMM and copy issued (communication first), both completed.
+Every round runs, in this order, the isolated GEMM, then per mover the isolated copy and the
+concurrent step, so clock and thermal drift hit isolated and concurrent times alike. Before
+every run, untimed: outputs poisoned, then the library reads 512 MiB of scratch (Infinity Cache
+flush) before its clock starts. After every run, untimed: each destination range is compared
+byte for byte with its source on the device (the copy's definition) and C bit for bit with the
+isolated GEMM's C. The CPU oracle runs only in the cpu_baseline leg: it computes a bounded
+sample of C's rows (timed), which are then compared with the GPU's rows (untimed).
 
-Prints ONE JSON line on stdout. Progress goes to stderr.
+Other modes print one JSON line per measured cell:
+  --mode movers    isolated copy GB/s vs size, CU mover variants and SDMA engine/chunk counts
+  --mode grid      the GC-equal workload's gather-size sweep: mover x GEMM CU mask x order
+  --mode cus       isolated GEMM time and CU-copy GB/s under balanced CU masks
+
+Prints ONE JSON line on stdout in the default mode. Progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -34,11 +43,31 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_source_hash() -> str:
+    path = os.path.join(ROOT, "concurrent_gemm_dma_amd", "csrc", "gemm.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def measured_traffic(kernel: str, w):
+    """HBM-side bytes per launch of `kernel` on workload `w`, from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE record (each scaled by its calibration against a copy kernel of
+    known size), or None when there is no record or the kernel source changed since it was
+    taken."""
+    path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(f"{kernel}@{w.name}")
+    if not rec or rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return int(rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"])
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--mode", default="c3", choices=["c3", "movers", "grid", "cus"])
     p.add_argument("--workload", type=int, default=2, help="workload id (1..5)")
     p.add_argument("--gather-mib", type=int, default=0, help="workload 5: total gather MiB")
     p.add_argument("--keep-per-xcc", type=int, default=0,
@@ -47,104 +76,126 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--profile", action="store_true",
-                   help="few steps, no verification or CPU baseline (for rocprofv3 runs)")
+                   help="no verification or CPU baseline (for rocprofv3 runs)")
     return p.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
-        log("bench.py: only --gpus 1 is supported (single-GPU build)")
-        sys.exit(2)
-    if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
-        log("bench.py: launched with WORLD_SIZE > 1; this build runs on one GPU only")
-        sys.exit(2)
+class Setup:
+    """Seeded inputs of one workload resident in HBM, plus the per-run checks."""
 
+    def __init__(self, c3, w, with_gemm=True, check=True):
+        import numpy as np
+        import torch
+
+        from concurrent_gemm_dma_amd import workloads as wl
+
+        self.c3, self.w, self.torch, self.np, self.check = c3, w, torch, np, check
+        dev = torch.device("cuda:0")
+        t0 = time.time()
+        if with_gemm:
+            self.A, self.B = wl.gen_gemm_operands(w)
+            self.dA = torch.from_numpy(self.A.view(np.int16)).to(dev)
+            self.dB = torch.from_numpy(self.B.view(np.int16)).to(dev)
+            self.dC = torch.empty((w.M, w.N), dtype=torch.int16, device=dev)
+            self.gargs = c3.gemm_args(self.dA, self.dB, self.dC, w.M, w.N, w.K)
+        self.iso_c = None
+        if w.copy == "gather":
+            self.dsrc = [torch.from_numpy(s).to(dev) for s in wl.gen_shards(w)]
+            total = w.units * w.unit_bytes
+        else:
+            self.dsrc = torch.from_numpy(wl.gen_a2a_source(w)).to(dev)
+            total = w.units * w.units * w.unit_bytes
+        self.ddst = torch.empty(total, dtype=torch.uint8, device=dev)
+        self.poison_i = 0
+        torch.cuda.synchronize()
+        log(f"{w.name}: inputs resident in HBM in {time.time() - t0:.1f} s")
+
+    def cargs(self, mover, opts=None):
+        w = self.w
+        if w.copy == "gather":
+            return self.c3.gather_args(self.ddst, self.dsrc, w.unit_bytes, mover, opts)
+        return self.c3.all2all_args(self.ddst, self.dsrc, w.units, w.unit_bytes, mover, opts)
+
+    def poison(self):
+        self.poison_i += 1
+        if hasattr(self, "dC"):
+            self.dC.fill_(-1 - (self.poison_i % 7))
+        self.ddst.fill_((0xA5 + self.poison_i) & 0xFF)
+        self.torch.cuda.synchronize()
+
+    def verify_copy(self, label):
+        """Every destination range equals its source range, byte for byte (on the device)."""
+        if not self.check:
+            return
+        w, teq = self.w, self.torch.equal
+        if w.copy == "gather":
+            sb = w.unit_bytes
+            for i, s in enumerate(self.dsrc):
+                if not teq(self.ddst[i * sb:(i + 1) * sb], s):
+                    raise SystemExit(f"{label}: gather shard {i} differs from its destination range")
+        else:
+            g, bb = w.units, w.unit_bytes
+            for i in range(g):
+                for j in range(g):
+                    src = self.dsrc[(i * g + j) * bb:(i * g + j + 1) * bb]
+                    dst = self.ddst[(j * g + i) * bb:(j * g + i + 1) * bb]
+                    if not teq(src, dst):
+                        raise SystemExit(f"{label}: all-to-all block ({i},{j}) misplaced")
+
+    def verify_c(self, label):
+        """C is bit-identical to the first isolated GEMM's C (deterministic kernel)."""
+        if self.iso_c is None:
+            self.iso_c = self.dC.clone()
+        elif self.check and not self.torch.equal(self.dC, self.iso_c):
+            raise SystemExit(f"{label}: C differs from the isolated GEMM")
+
+
+def cpu_baseline_and_parity(args, s, w, oracle_seconds):
+    """The oracle as it stands, on a bounded sample of the workload (rows 0..r-1 of C, sized to
+    take about `oracle_seconds` on the host cores), timed; then those rows are compared with the
+    GPU's C (|d| <= 1e-2 max(1,|ref|) elementwise, relative Frobenius <= 1e-3)."""
     import numpy as np
-    import torch
 
     import oracle
-    from concurrent_gemm_dma_amd import _c3 as c3
+
+    nthreads = oracle.threads(0)
+    t1 = time.time()
+    oracle.gemm_f32acc(s.A, s.B, rows=(0, 1))
+    dt = max(time.time() - t1, 1e-3)
+    r = int(max(1, min(w.M, oracle_seconds / dt)))
+    t1 = time.time()
+    ref = oracle.gemm_f32acc(s.A, s.B, rows=(0, r))
+    dt = time.time() - t1
+    got = s.iso_c[:r].cpu().numpy().view(np.uint16)
+    rep = oracle.gemm_compare(ref, got)
+    if not oracle.gemm_within_tolerance(rep):
+        raise SystemExit(f"GEMM parity failure vs oracle on rows 0..{r - 1}: {rep}")
+    log(f"oracle rows 0..{r - 1}: GPU C within tolerance ({rep['n_diff']} of {rep['n']} elements "
+        f"differ by rounding, max scaled err {rep['max_scaled_err']:.2e})")
+    cpu = {"value": round(2.0 * r * w.N * w.K / dt / 1e12, 6), "unit": "TFLOP/s",
+           "cores": nthreads, "kind": "oracle",
+           "sample": f"fp32-accumulate triple-loop GEMM oracle, rows 0..{r - 1} of C "
+                     f"({r}x{w.N}x{w.K}, {2.0 * r * w.N * w.K / 1e9:.1f} GFLOP) in {dt:.1f} s"}
+    parity = {"rows": r, "elements": rep["n"], "differ_by_rounding": rep["n_diff"],
+              "max_scaled_err": rep["max_scaled_err"], "frob_rel": rep["frob_rel"]}
+    return cpu, parity
+
+
+def run_c3(args, c3, info):
     from concurrent_gemm_dma_amd import workloads as wl
 
-    dev = torch.device("cuda:0")
-    c3.c3_init(0)
-    info = c3.c3_device_info()
-    log("device:", info)
     w = wl.WORKLOADS[args.workload]
     if args.gather_mib:
         w = w.with_gather_total(args.gather_mib * MiB)
     M, N, K = w.M, w.N, w.K
     flops = w.gemm_flops
     copy_bytes = w.copy_bytes  # payload S; HBM traffic of the copy is 2S (read + write)
-
-    # ---- inputs (seeded, synthetic), resident in HBM before any timing ----
-    t0 = time.time()
-    A, B = wl.gen_gemm_operands(w)
-    if w.copy == "gather":
-        src_np = wl.gen_shards(w)
-        want = oracle.gather(src_np)
-    else:
-        src_np = wl.gen_a2a_source(w)
-        want = oracle.all2all_block(src_np, w.units, w.unit_bytes)
-    dA = torch.from_numpy(A.view(np.int16)).to(dev)
-    dB = torch.from_numpy(B.view(np.int16)).to(dev)
-    dC = torch.empty((M, N), dtype=torch.int16, device=dev)
-    if w.copy == "gather":
-        dsrc = [torch.from_numpy(s).to(dev) for s in src_np]
-    else:
-        dsrc = torch.from_numpy(src_np).to(dev)
-    ddst = torch.empty(want.size, dtype=torch.uint8, device=dev)
-    dwant = torch.from_numpy(want).to(dev)
-    torch.cuda.synchronize()
-    log(f"inputs ready in {time.time() - t0:.1f} s")
-
-    rows, cols = wl.sample_indices(M, N, 512, seed=w.wid, full_rows=(M // 2,))
-    _, ref64, _ = (None, None, None) if args.profile else oracle.gemm_elems(A, B, rows, cols)
+    s = Setup(c3, w, check=not args.profile)
 
     gmask = c3.c3_cu_mask_balanced(args.keep_per_xcc) if args.keep_per_xcc else None
     comm_first = not args.gemm_first
-
-    def cargs(mover):
-        if w.copy == "gather":
-            return c3.gather_args(ddst, dsrc, w.unit_bytes, mover)
-        return c3.all2all_args(ddst, dsrc, w.units, w.unit_bytes, mover)
-
-    gargs = c3.gemm_args(dA, dB, dC, M, N, K)
-    poison_i = [0]
-
-    def poison():
-        poison_i[0] += 1
-        dC.fill_(-1 - (poison_i[0] % 7))
-        ddst.fill_((0xA5 + poison_i[0]) & 0xFF)
-        torch.cuda.synchronize()
-
-    iso_c = None
-
-    def verify_copy(label):
-        if args.profile:
-            return
-        if not torch.equal(ddst, dwant):
-            host = ddst.cpu().numpy()
-            raise SystemExit(f"{label}: copy mismatch at byte {oracle.first_diff(want, host)}")
-
-    def verify_c(label):
-        nonlocal iso_c
-        if iso_c is None:
-            iso_c = dC.clone()
-            if not args.profile:
-                got = iso_c.cpu().numpy().view(np.uint16)[rows, cols]
-                rep = oracle.gemm_compare(ref64, got)
-                if not oracle.gemm_within_tolerance(rep):
-                    raise SystemExit(f"GEMM parity failure vs oracle: {rep}")
-                log(f"GEMM sampled parity vs oracle ok ({rep['n']} elems, "
-                    f"{rep['n_diff']} differ by one rounding)")
-        elif not args.profile and not torch.equal(dC, iso_c):
-            raise SystemExit(f"{label}: C differs from the isolated GEMM")
-
     movers = (("sdma", c3.C3_MOVER_SDMA), ("cu", c3.C3_MOVER_CU))
-    copy_args = {name: cargs(mv) for name, mv in movers}
+    copy_args = {name: s.cargs(mv) for name, mv in movers}
     conc = {}
     for name, mv in movers:
         cmask = None
@@ -155,36 +206,35 @@ def main():
     iso_g_opts = c3.conc_opts(gemm_mask=gmask, flush_bytes=FLUSH_BYTES)
     iso_c_opts = c3.conc_opts(flush_bytes=FLUSH_BYTES)
 
-    # Every round runs the isolated GEMM, then per mover the isolated copy and the concurrent
-    # step, so that clock and thermal drift affect isolated and concurrent times alike.
     t_gemm, g_gpu = [], []
     rec = {name: {"t_copy": [], "c_gpu": [], "t_conc": [], "gk": []} for name, _ in movers}
+    torch = s.torch
     torch.cuda.synchronize()
-    wall0 = None
+    wall0 = time.time()
     for i in range(args.warmup + args.steps):
         if i == args.warmup:
             torch.cuda.synchronize()
             wall0 = time.time()
         timed = i >= args.warmup
-        poison()
-        t = c3.c3_run_concurrent(gargs, None, iso_g_opts)
-        verify_c(f"isolated GEMM {i}")
+        s.poison()
+        t = c3.c3_run_concurrent(s.gargs, None, iso_g_opts)
+        s.verify_c(f"isolated GEMM {i}")
         if timed:
             t_gemm.append(t["t_conc_ns"] * 1e-9)
             g_gpu.append(t["gemm_gpu_ms"] * 1e-3)
-        for name, mv in movers:
+        for name, _ in movers:
             ca = copy_args[name][0]
             r = rec[name]
-            poison()
+            s.poison()
             t = c3.c3_run_concurrent(None, ca, iso_c_opts)
-            verify_copy(f"isolated {name} copy {i}")
+            s.verify_copy(f"isolated {name} copy {i}")
             if timed:
                 r["t_copy"].append(t["t_conc_ns"] * 1e-9)
                 r["c_gpu"].append(t["copy_gpu_ms"] * 1e-3)
-            poison()
-            t = c3.c3_run_concurrent(gargs, ca, conc[name])
-            verify_copy(f"{name} step {i}")
-            verify_c(f"{name} step {i}")
+            s.poison()
+            t = c3.c3_run_concurrent(s.gargs, ca, conc[name])
+            s.verify_copy(f"{name} step {i}")
+            s.verify_c(f"{name} step {i}")
             if timed:
                 r["t_conc"].append(t["t_conc_ns"] * 1e-9)
                 r["gk"].append(t["gemm_gpu_ms"] * 1e-3)
@@ -195,6 +245,7 @@ def main():
         f"{flops / statistics.median(g_gpu) / 1e12:.1f} TFLOP/s events)")
 
     results = {}
+    best_copy = min(statistics.median(rec[name]["t_copy"]) for name, _ in movers)
     for name, _ in movers:
         r = rec[name]
         T_copy = statistics.median(r["t_copy"])
@@ -212,6 +263,7 @@ def main():
             "gemm_tflops_concurrent": flops / T_conc / 1e12,
             "copy_gbps_concurrent": 2 * copy_bytes / T_conc / 1e9,
             "gemm_kernel_ms_concurrent": statistics.mean(r["gk"]) * 1e3,
+            "speedup_vs_best_serial": (T_gemm + best_copy) / T_conc,
             **{k: m[k] for k in ("ideal_speedup", "speedup", "uplift_fraction", "ratio_of_ideal",
                                  "gemm_slowdown", "hbm_ceiling", "taxonomy")},
         }
@@ -222,35 +274,22 @@ def main():
     # ---- roofline of the dominant kernel (the GEMM): HIP events recorded by the library on the
     # GEMM's own stream around every launch of the timed SDMA-concurrent steps ----
     gemm_kernel_s = statistics.mean(rec["sdma"]["gk"])
-    achieved_tflops = flops / gemm_kernel_s / 1e12
-    roofline = {"bound": "mfma" if M > 64 else "hbm",
-                "achieved": None, "peak": None, "unit": None, "frac": None, "traffic": None}
+    roofline = {"bound": "mfma" if M > 64 else "hbm"}
     if M > 64:
-        roofline.update(achieved=round(achieved_tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                        frac=round(achieved_tflops / PEAK_BF16_TFLOPS, 4))
+        a = flops / gemm_kernel_s / 1e12
+        roofline.update(achieved=round(a, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                        frac=round(a / PEAK_BF16_TFLOPS, 4))
     else:
-        gbps = w.gemm_bytes / gemm_kernel_s / 1e9
-        roofline.update(achieved=round(gbps, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
-                        frac=round(gbps / PEAK_HBM_GBPS, 4))
-    roofline["kernel"] = "gemm_bf16_tile256" if M > 64 else "gemm_bf16_skinny (+splitk_reduce)"
+        a = w.gemm_bytes / gemm_kernel_s / 1e9
+        roofline.update(achieved=round(a, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
+                        frac=round(a / PEAK_HBM_GBPS, 4))
+    roofline["kernel"] = "gemm_bf16_tile256_dma" if M > 64 else "gemm_bf16_skinny (+splitk_reduce)"
+    roofline["traffic"] = measured_traffic(roofline["kernel"], w)
     roofline["kernel_ms"] = round(gemm_kernel_s * 1e3, 4)
 
-    # ---- CPU baseline: the oracle as it stands, on a bounded sample of the same workload ----
-    cpu = None
+    cpu, parity = None, None
     if not args.no_cpu_baseline and not args.profile:
-        nthreads = oracle.threads(0)
-        r = 1
-        t1 = time.time()
-        oracle.gemm_f32acc(A, B, rows=(0, r))
-        dt = max(time.time() - t1, 1e-3)
-        r = int(max(1, min(M, args.cpu_seconds / dt)))
-        t1 = time.time()
-        oracle.gemm_f32acc(A, B, rows=(0, r))
-        dt = time.time() - t1
-        cpu = {"value": round(2.0 * r * N * K / dt / 1e12, 6), "unit": "TFLOP/s",
-               "cores": nthreads, "kind": "oracle",
-               "sample": f"fp32-accumulate triple-loop GEMM oracle, rows 0..{r - 1} of C "
-                         f"({r}x{N}x{K}, {2.0 * r * N * K / 1e9:.1f} GFLOP) in {dt:.1f} s"}
+        cpu, parity = cpu_baseline_and_parity(args, s, w, args.cpu_seconds)
         log("cpu baseline:", cpu)
 
     head = results["sdma"]
@@ -266,11 +305,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded; bf16 N(0,1) activations, N(0,0.02) weights; copy payload as the workload states)",
+        "data": "synthetic (seeded; bf16 N(0,1) activations, N(0,0.02) weights; copy payload as "
+                "the workload states)",
         "config": {
             "workload": f"{w.name}: bf16 GEMM {M}x{N}x{K} || {w.copy} "
                         f"{w.units}{'x' + str(w.units) if w.copy == 'all2all' else ''} x "
-                        f"{w.unit_bytes // MiB} MiB; value = SDMA mover, "
+                        f"{w.unit_bytes / MiB:g} MiB; value = SDMA mover, "
                         f"{'comm-first' if comm_first else 'GEMM-first'}, "
                         f"GEMM CUs {'all' if not gmask else str(args.keep_per_xcc) + '/XCC'}",
             "M": M, "N": N, "K": K, "copy_bytes": copy_bytes,
@@ -287,14 +327,176 @@ def main():
                    for k, v in results.items()},
         "timing": "ms_per_step = mean over the timed steps of the library's host clock from the "
                   "first issue to both operations complete (SDMA cell); isolated and concurrent "
-                  "runs interleaved per step, each after a poison + 512 MiB cache flush",
+                  "runs interleaved per step, each after a poison + 512 MiB read flush",
         "wall_s_timed_rounds": round(wall, 3),
-        "verified": "every step: copy byte-exact vs oracle, C bit-identical to isolated C; "
-                    "isolated C vs oracle on sampled elements",
+        "verified": "every run: each copy destination range equal to its source (device compare), "
+                    "C bit-identical to the isolated C; isolated C vs the CPU oracle on the "
+                    "cpu_baseline rows",
+        "gemm_parity_vs_oracle": parity,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def time_copy(c3, s, mover, opts, reps, conc_opts=None):
+    ca, _keep = s.cargs(mover, opts)
+    ts, gs, eng = [], [], 0
+    o = conc_opts if conc_opts is not None else c3.conc_opts(flush_bytes=FLUSH_BYTES)
+    for i in range(reps + 1):
+        s.poison()
+        t = c3.c3_run_concurrent(None, ca, o)
+        s.verify_copy("mover sweep")
+        if i:
+            ts.append(t["t_conc_ns"] * 1e-9)
+            gs.append(t["copy_gpu_ms"] * 1e-3)
+            eng = t["engines_used"]
+    return statistics.median(ts), statistics.median(gs), eng, t["n_chunks"]
+
+
+def run_movers(args, c3, info):
+    """Isolated copy throughput against size (the paper's Fig. 9 question on one GPU)."""
+    from concurrent_gemm_dma_amd import workloads as wl
+
+    base = wl.WORKLOADS[5]
+    engines = [1 << b for b in range(32) if info["sdma_engine_mask"] >> b & 1]
+    reps = max(3, args.steps)
+    for total_mib in (1, 4, 16, 64, 128, 256, 512, 1024):
+        w = base.with_gather_total(total_mib * MiB)
+        s = Setup(c3, w, with_gemm=False, check=not args.profile)
+        S = w.copy_bytes
+        cells = [("cu", "default", c3.C3_MOVER_CU, c3.move_opts()),
+                 ("cu", "nontemporal", c3.C3_MOVER_CU, c3.move_opts(nontemporal=1))]
+        for n in (1, 2, 4, 8, 16):
+            if n <= len(engines):
+                mask = sum(engines[:n])
+                cells.append(("sdma", f"{n} engines, 8 chunks", c3.C3_MOVER_SDMA,
+                              c3.move_opts(engine_mask=mask)))
+        for chunks in (16, 32, 64):
+            cells.append(("sdma", f"{len(engines)} engines, {chunks} chunks", c3.C3_MOVER_SDMA,
+                          c3.move_opts(chunk_bytes=max(4096, S // chunks))))
+        for mover, label, mv, opts in cells:
+            T, G, eng, nch = time_copy(c3, s, mv, opts, reps)
+            print(json.dumps({"mode": "movers", "total_mib": total_mib, "mover": mover,
+                              "variant": label, "chunks": nch, "engines_used": eng,
+                              "t_ms_host": round(T * 1e3, 4), "t_ms_device": round(G * 1e3, 4),
+                              "gbps_2S_host": round(2 * S / T / 1e9, 1),
+                              "gbps_2S_device": round(2 * S / G / 1e9, 1) if G > 0 else None}),
+                  flush=True)
+        del s
+
+
+def run_grid(args, c3, info):
+    """The GC-equal workload's sweep: gather size x mover x GEMM CU mask x issue order."""
+    from concurrent_gemm_dma_amd import workloads as wl
+
+    base = wl.WORKLOADS[5]
+    per = info["n_cu"] // info["n_xcc"]
+    keeps = (per, per * 7 // 8, per * 3 // 4)
+    reps = max(3, args.steps)
+    for total in base.sweep_total_bytes:
+        w = base.with_gather_total(total)
+        s = Setup(c3, w, check=not args.profile)
+        copy_bytes = w.copy_bytes
+        rounds = []
+        for i in range(reps + 1):
+            rnd = {}
+            s.poison()
+            rnd["gemm"] = c3.c3_run_concurrent(s.gargs, None, c3.conc_opts(flush_bytes=FLUSH_BYTES))["t_conc_ns"]
+            s.verify_c("grid isolated GEMM")
+            for mname, mv in (("cu", c3.C3_MOVER_CU), ("sdma", c3.C3_MOVER_SDMA)):
+                ca, _keep = s.cargs(mv)
+                s.poison()
+                rnd[("copy", mname)] = c3.c3_run_concurrent(None, ca, c3.conc_opts(flush_bytes=FLUSH_BYTES))["t_conc_ns"]
+                s.verify_copy("grid isolated copy")
+                for keep in keeps:
+                    gm = None if keep == per else c3.c3_cu_mask_balanced(keep)
+                    cm = None if (keep == per or mv == c3.C3_MOVER_SDMA) else c3.c3_cu_mask_balanced(keep, True)
+                    for cf in (False, True):
+                        s.poison()
+                        t = c3.c3_run_concurrent(s.gargs, ca, c3.conc_opts(
+                            gemm_mask=gm, comm_mask=cm, comm_first=cf, flush_bytes=FLUSH_BYTES))
+                        s.verify_copy("grid step")
+                        s.verify_c("grid step")
+                        rnd[("conc", mname, keep, cf)] = t["t_conc_ns"]
+            if i:
+                rounds.append(rnd)
+        Tg = statistics.median(r["gemm"] for r in rounds) * 1e-9
+        best_copy = min(statistics.median(r[("copy", m)] for r in rounds) for m in ("cu", "sdma")) * 1e-9
+        for mname in ("cu", "sdma"):
+            Tc = statistics.median(r[("copy", mname)] for r in rounds) * 1e-9
+            for keep in keeps:
+                for cf in (False, True):
+                    Tconc = statistics.mean(r[("conc", mname, keep, cf)] for r in rounds) * 1e-9
+                    m = c3.c3_derive_metrics(Tg, Tc, Tconc, float(w.gemm_bytes + 2 * copy_bytes),
+                                             PEAK_HBM_GBPS * 1e9)
+                    print(json.dumps({
+                        "mode": "grid", "gather_mib": total // MiB, "mover": mname,
+                        "gemm_cus_per_xcc": keep, "comm_first": cf,
+                        "t_gemm_ms": round(Tg * 1e3, 4), "t_copy_ms": round(Tc * 1e3, 4),
+                        "t_conc_ms": round(Tconc * 1e3, 4),
+                        # against the faster mover's serial time, so that a slow mover cannot
+                        # look good by inflating its own serial baseline
+                        "speedup_vs_best_serial": round((Tg + best_copy) / Tconc, 4),
+                        "gemm_tflops_concurrent": round(w.gemm_flops / Tconc / 1e12, 1),
+                        **{k: (round(v, 4) if isinstance(v, float) else v) for k, v in m.items()}}),
+                        flush=True)
+        del s
+
+
+def run_cus(args, c3, info):
+    """Isolated GEMM time and CU-copy throughput with only k CUs per XCC (Fig. 5 analog)."""
+    from concurrent_gemm_dma_amd import workloads as wl
+
+    per = info["n_cu"] // info["n_xcc"]
+    reps = max(3, args.steps)
+    for wid in (2, 3, 5):
+        w = wl.WORKLOADS[wid]
+        s = Setup(c3, w, check=not args.profile)
+        for keep in (per, per * 7 // 8, per * 3 // 4, per // 2, per // 4, per // 8):
+            gm = None if keep == per else c3.c3_cu_mask_balanced(keep)
+            ts = []
+            for i in range(reps + 1):
+                s.poison()
+                t = c3.c3_run_concurrent(s.gargs, None, c3.conc_opts(gemm_mask=gm, flush_bytes=FLUSH_BYTES))
+                s.verify_c("cus GEMM")
+                if i:
+                    ts.append(t["gemm_gpu_ms"] * 1e-3)
+            T = statistics.median(ts)
+            ca, _keep = s.cargs(c3.C3_MOVER_CU)
+            tc = []
+            for i in range(reps + 1):
+                s.poison()
+                t = c3.c3_run_concurrent(None, ca, c3.conc_opts(comm_mask=gm, flush_bytes=FLUSH_BYTES))
+                s.verify_copy("cus copy")
+                if i:
+                    tc.append(t["copy_gpu_ms"] * 1e-3)
+            Tc = statistics.median(tc)
+            print(json.dumps({"mode": "cus", "workload": w.name, "cus_per_xcc": keep,
+                              "gemm_ms": round(T * 1e3, 4),
+                              "gemm_tflops": round(w.gemm_flops / T / 1e12, 1),
+                              "gemm_gbps": round(w.gemm_bytes / T / 1e9, 1),
+                              "cu_copy_ms": round(Tc * 1e3, 4),
+                              "cu_copy_gbps_2S": round(2 * w.copy_bytes / Tc / 1e9, 1)}), flush=True)
+        del s
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        log("bench.py: only --gpus 1 is supported (single-GPU build)")
+        sys.exit(2)
+    if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
+        log("bench.py: launched with WORLD_SIZE > 1; this build runs on one GPU only")
+        sys.exit(2)
+
+    from concurrent_gemm_dma_amd import _c3 as c3
+
+    c3.c3_init(0)
+    info = c3.c3_device_info()
+    log("device:", info)
+    {"c3": run_c3, "movers": run_movers, "grid": run_grid, "cus": run_cus}[args.mode](args, c3, info)
     c3.c3_finalize()
 
 

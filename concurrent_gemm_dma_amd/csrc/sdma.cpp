@@ -171,10 +171,21 @@ c3_status sdma_issue(const std::vector<Segment>& segs, const c3_move_opts& o, Sd
         char* dst;
         uint64_t bytes;
     };
+    // Default split: one transfer per segment (shard or block), each cut into just enough
+    // pieces that there are at least as many transfers as engines (one engine moves only
+    // ~100 GB/s, so a gather of 8 shards would otherwise leave half of 16 engines idle).
+    size_t nonempty = 0;
+    for (const Segment& s : segs) nonempty += s.bytes != 0;
+    const uint64_t pieces =
+        nonempty ? std::max<uint64_t>(1, (engines.size() + nonempty - 1) / nonempty) : 1;
     std::vector<Chunk> chunks;
     for (const Segment& s : segs) {
         if (s.bytes == 0) continue;
-        const uint64_t step = o.chunk_bytes ? o.chunk_bytes : s.bytes;
+        uint64_t step = o.chunk_bytes;
+        if (!step) {
+            step = (s.bytes + pieces - 1) / pieces;
+            step = (step + 255) & ~uint64_t(255);  // 256-byte multiples keep pieces aligned
+        }
         for (uint64_t off = 0; off < s.bytes; off += step)
             chunks.push_back({static_cast<const char*>(s.src) + off, static_cast<char*>(s.dst) + off,
                               std::min(step, s.bytes - off)});

@@ -93,7 +93,9 @@ typedef struct {
 /* Options for one data movement. Zero-initialised means defaults. */
 typedef struct {
     uint64_t chunk_bytes;  /* SDMA: split every segment into chunks of at most this many bytes
-                              (0 = one transfer per shard or block, the paper's direct scheme) */
+                              (0 = one transfer per shard or block, the paper's direct scheme,
+                              each cut into equal 256-byte-multiple pieces until there are at
+                              least as many transfers as engines) */
     uint32_t engine_mask;  /* SDMA: use only these engines (one-hot HSA_AMD_SDMA_ENGINE_i bits;
                               0 = every engine available for device-local copies). Chunk c goes
                               to the (c mod n)-th engine of the mask. */
@@ -135,8 +137,10 @@ typedef struct {
     int32_t comm_first;   /* 1 = issue the communication before the GEMM */
     int32_t use_priority; /* must be 0: every stream stays at default priority; the
                              prioritization control is the issue order (comm_first) */
-    uint64_t flush_bytes; /* > 0: before the timed region, overwrite this many bytes of a
-                             library scratch buffer to evict the last-level (Infinity) cache */
+    uint64_t flush_bytes; /* > 0: before the timed region, read this many bytes of a library
+                             scratch buffer through the caches, evicting the last-level
+                             (Infinity) cache; dirty lines are written back then, not in the
+                             timed run (at least 32 KiB, else no flush) */
 } c3_conc_opts;
 
 /* Timings of one run. Host times use a monotonic clock and start just before the first issue. */
@@ -243,8 +247,9 @@ c3_status c3_gather(void* dst, const void* const* shards, int n_shards, size_t s
 c3_status c3_all2all_block(void* dst, const void* src, int grid, size_t block_bytes,
                            c3_mover mover, const c3_move_opts* opt, void* stream);
 
-/* Overwrite `bytes` of a library-owned scratch buffer on `stream` (evicts the Infinity Cache).
- * Allocates the scratch on first use or growth. */
+/* Read `bytes` of a library-owned scratch buffer on `stream`, which evicts the Infinity Cache
+ * and leaves it holding clean lines (writes one word per workgroup into the scratch's first
+ * 8 KiB). Allocates the scratch on first use or growth; below 32 KiB nothing is done. */
 c3_status c3_flush_llc(size_t bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------

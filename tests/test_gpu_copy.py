@@ -112,20 +112,34 @@ def test_sdma_fault_hooks(c3gpu):
     sb = 256 * KiB
     shards = [wl.gen_bytes(sb, 8500 + i) for i in range(8)]
     want = oracle.gather(shards)
+    # one chunk per shard (chunk_bytes = shard size), so chunk i is shard i
     # dropped transfer: call succeeds, the byte-exact check must catch the stale chunk 3
     got, _ = do_gather(c3gpu, shards, "sdma",
-                       c3gpu.move_opts(fault_mode=c3gpu.C3_FAULT_DROP_CHUNK, fault_chunk=3))
+                       c3gpu.move_opts(chunk_bytes=sb, fault_mode=c3gpu.C3_FAULT_DROP_CHUNK,
+                                       fault_chunk=3))
     off = oracle.first_diff(want, got)
     assert 3 * sb <= off < 4 * sb
     assert oracle.first_diff(want[4 * sb:], got[4 * sb:]) == -1
+    # default split (16 transfers over 16 engines): dropping transfer 7 loses the second half
+    # of shard 3
+    got, _ = do_gather(c3gpu, shards, "sdma",
+                       c3gpu.move_opts(fault_mode=c3gpu.C3_FAULT_DROP_CHUNK, fault_chunk=7))
+    off = oracle.first_diff(want, got)
+    n_eng = bin(c3gpu.c3_device_info()["sdma_engine_mask"]).count("1")
+    if n_eng == 16:
+        assert 3 * sb + sb // 2 <= off < 4 * sb
+    else:
+        assert off != -1
     # stuck transfer: timeout, after every real chunk completed
     with pytest.raises(c3gpu.C3Error) as e:
-        do_gather(c3gpu, shards, "sdma", c3gpu.move_opts(fault_mode=c3gpu.C3_FAULT_STUCK_CHUNK,
+        do_gather(c3gpu, shards, "sdma", c3gpu.move_opts(chunk_bytes=sb,
+                                                         fault_mode=c3gpu.C3_FAULT_STUCK_CHUNK,
                                                          fault_chunk=5, timeout_ms=300))
     assert e.value.status == c3gpu.C3_E_TIMEOUT
     # failed transfer (negative completion signal): reported as an HSA error
     with pytest.raises(c3gpu.C3Error) as e:
-        do_gather(c3gpu, shards, "sdma", c3gpu.move_opts(fault_mode=c3gpu.C3_FAULT_ERROR_CHUNK,
+        do_gather(c3gpu, shards, "sdma", c3gpu.move_opts(chunk_bytes=sb,
+                                                         fault_mode=c3gpu.C3_FAULT_ERROR_CHUNK,
                                                          fault_chunk=0))
     assert e.value.status == c3gpu.C3_E_HSA
     # the library is still usable afterwards
