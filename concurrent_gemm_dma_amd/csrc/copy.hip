@@ -18,13 +18,14 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kSegPerLaunch = 64;
 constexpr int kThreads = 256;
-// 4 pieces in flight per lane and 32 KiB per workgroup measured fastest on MI355X (5.9 TB/s of
-// read + write for a 1 GiB gather, against 5.5 TB/s for 8 pieces and 64 KiB).
+// One piece per lane per pass and 8 KiB per workgroup measured fastest on MI355X (6.27 TB/s of
+// read + write for a 1 GiB gather; 5.9 TB/s for 4 pieces and 32 KiB, 5.5 TB/s for 8 and 64 KiB):
+// many small workgroups keep more requests in flight across the chip than few long ones.
 #ifndef C3_COPY_UNROLL
-#define C3_COPY_UNROLL 4
+#define C3_COPY_UNROLL 1
 #endif
 #ifndef C3_COPY_BLOCK_KIB
-#define C3_COPY_BLOCK_KIB 32
+#define C3_COPY_BLOCK_KIB 8
 #endif
 constexpr int kUnroll = C3_COPY_UNROLL;
 constexpr uint64_t kPiecesPerIter = (uint64_t)kThreads * kUnroll;  // 16-byte pieces
