@@ -18,6 +18,10 @@ Parity status of each routine (pins are in the CPU test suite):
                       within the recursive-summation bound, identity / zero / integer-exact
   gemm_f64acc         pinned: exact integer products (numpy int64), fp64 brute force
   gather / all2all    pinned: per-byte Python loops, involution, diagonal invariance
+  reduce_sum_bf16     pinned: exact integer sums, exhaustive two-rank sums against exact rational
+                      sums rounded by the independent bf16 formulation, hand-worked order /
+                      single-rounding / signed-zero cases, the fp32 summation error bound
+  allreduce_local     pinned: slot placement by per-element loops, rank variation
   checkers            pinned: planted mistakes (dropped chunk, flipped byte, swapped shards)
   (mutants)           mistakes planted in a scratch copy of oracle.c fail the pins above
   metrics             pinned: closed forms (S_ideal in [1, 2], = 2 iff equal times)
@@ -103,6 +107,13 @@ def load_library(path: str):
     L.orc_all2all_block.restype = None
     L.orc_all2all_block.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.c_size_t]
+    L.orc_reduce_sum_bf16.restype = None
+    L.orc_reduce_sum_bf16.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                      ctypes.c_size_t, _u16p]
+    L.orc_allreduce_local.restype = None
+    L.orc_allreduce_local.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                      ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_size_t, _u16p, _u16p]
     L.orc_first_diff.restype = ctypes.c_int64
     L.orc_first_diff.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
     L.orc_gemm_compare.restype = None
@@ -235,6 +246,51 @@ def all2all_block(src: np.ndarray, grid: int, block_bytes: int) -> np.ndarray:
     dst = np.empty_like(s)
     lib().orc_all2all_block(dst.ctypes.data, s.ctypes.data, grid, block_bytes)
     return dst
+
+
+# ---------------------------------------------------------------------------------------------
+# All-reduce local share
+# ---------------------------------------------------------------------------------------------
+
+def _u16_views(arrays: Sequence[np.ndarray], n: int, what: str) -> list:
+    views = [np.ascontiguousarray(a).view(np.uint16).reshape(-1) for a in arrays]
+    if any(v.size != n for v in views):
+        raise ValueError(f"{what}: every array must hold {n} bf16 elements")
+    return views
+
+
+def reduce_sum_bf16(contribs: Sequence[np.ndarray]) -> np.ndarray:
+    """Reduce-scatter local share: elementwise fp32 sum of the ranks' bf16 contributions in rank
+    order, rounded once to bf16 (uint16 bit patterns)."""
+    if not contribs:
+        raise ValueError("reduce_sum_bf16 needs at least one contribution")
+    n = np.asarray(contribs[0]).view(np.uint16).size
+    views = _u16_views(contribs, n, "reduce_sum_bf16")
+    out = np.empty(n, dtype=np.uint16)
+    ptrs = (ctypes.c_void_p * len(views))(*[v.ctypes.data for v in views])
+    lib().orc_reduce_sum_bf16(ptrs, len(views), n, out)
+    return out
+
+
+def allreduce_local(contribs: Sequence[np.ndarray], peers: Sequence[np.ndarray | None],
+                    rank: int) -> tuple[np.ndarray, np.ndarray]:
+    """All-reduce local share: (reduced chunk, gathered result). peers[i] is rank i's reduced
+    chunk for i != rank; peers[rank] is ignored (may be None)."""
+    world = len(contribs)
+    if world < 1 or len(peers) != world or not 0 <= rank < world:
+        raise ValueError("allreduce_local: need world >= 1 contributions, world peers, 0 <= rank < world")
+    n = np.asarray(contribs[0]).view(np.uint16).size
+    cv = _u16_views(contribs, n, "allreduce_local contribs")
+    if any(peers[i] is None for i in range(world) if i != rank):
+        raise ValueError("allreduce_local: every peer other than rank needs a chunk")
+    pv = [None if peers[i] is None else _u16_views([peers[i]], n, "allreduce_local peers")[0]
+          for i in range(world)]
+    reduced = np.empty(n, dtype=np.uint16)
+    dst = np.empty(world * n, dtype=np.uint16)
+    cp = (ctypes.c_void_p * world)(*[v.ctypes.data for v in cv])
+    pp = (ctypes.c_void_p * world)(*[None if v is None else v.ctypes.data for v in pv])
+    lib().orc_allreduce_local(cp, pp, world, rank, n, reduced, dst)
+    return reduced, dst
 
 
 # ---------------------------------------------------------------------------------------------

@@ -179,6 +179,41 @@ void orc_all2all_block(void* dst, const void* src, int grid, size_t block_bytes)
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* All-reduce local share: reduce-scatter (arithmetic) then all-gather (copy)                   */
+/* ------------------------------------------------------------------------------------------ */
+
+/*
+ * Reduce-scatter local share: element e of this rank's chunk is the sum of the `world` ranks'
+ * contributions in[0][e], ..., in[world-1][e]. Reading taken (the pages give no precision or
+ * order): fp32 accumulation, starting from rank 0's value and adding ranks 1, 2, ... in order,
+ * one rounding to bf16 at the end.
+ */
+void orc_reduce_sum_bf16(const uint16_t* const* in, int world, size_t n, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < (int64_t)n; ++e) {
+        float acc = f32_from_bf16(in[0][e]);
+        for (int r = 1; r < world; ++r) {
+            acc = acc + f32_from_bf16(in[r][e]);
+        }
+        out[e] = orc_bf16_from_f32_bits(bits_from_f32(acc));
+    }
+}
+
+/*
+ * All-reduce local share = reduce-scatter, then all-gather of the reduced chunks: `reduced`
+ * receives this rank's reduced chunk; dst slot i (chunk_elems bf16 each) receives `reduced` for
+ * i == rank and the other ranks' reduced chunks peers[i] otherwise.
+ */
+void orc_allreduce_local(const uint16_t* const* contribs, const uint16_t* const* peers, int world,
+                         int rank, size_t chunk_elems, uint16_t* reduced, uint16_t* dst) {
+    orc_reduce_sum_bf16(contribs, world, chunk_elems, reduced);
+    for (int i = 0; i < world; ++i) {
+        const uint16_t* from = (i == rank) ? reduced : peers[i];
+        memcpy(dst + (size_t)i * chunk_elems, from, chunk_elems * sizeof(uint16_t));
+    }
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* Checkers                                                                                     */
 /* ------------------------------------------------------------------------------------------ */
 

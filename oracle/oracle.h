@@ -88,6 +88,28 @@ void orc_gather(void* dst, const void* const* shards, int n_shards, size_t shard
  */
 void orc_all2all_block(void* dst, const void* src, int grid, size_t block_bytes);
 
+/* ---- All-reduce local share (reduce-scatter + all-gather) ---- */
+
+/*
+ * DMA engines do no arithmetic, so an all-reduce is split into a reduce-scatter (the sum, on the
+ * compute units) and an all-gather of the reduced chunks (a copy, which the engines can do)
+ * (L3 Synthesis page on 2412.14335, section 3 "attack surface", Attack 1; Pith review, "Reading
+ * between the lines"). On one GPU only the local share exists.
+ *
+ * Reduce-scatter local share: out[e] = bf16_rne(fp32 sum of in[r][e]), the sum started from
+ * rank 0's value with ranks 1..world-1 added in order (reading taken: the pages fix neither
+ * precision nor order). world >= 1; n elements per rank.
+ */
+void orc_reduce_sum_bf16(const uint16_t* const* in, int world, size_t n, uint16_t* out);
+
+/*
+ * All-reduce local share: reduced = orc_reduce_sum_bf16(contribs); then dst slot i (chunk_elems
+ * elements) = reduced if i == rank, else peers[i] (the other ranks' reduced chunks; peers[rank]
+ * is not read).
+ */
+void orc_allreduce_local(const uint16_t* const* contribs, const uint16_t* const* peers, int world,
+                         int rank, size_t chunk_elems, uint16_t* reduced, uint16_t* dst);
+
 /* ---- Checkers ---- */
 
 /* Offset of the first differing byte, or -1 if the two ranges are equal. */

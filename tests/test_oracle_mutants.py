@@ -25,6 +25,13 @@ MUTANTS = {
                         "memcpy((unsigned char*)dst + (size_t)i * shard_bytes, shards[n_shards - 1 - i], shard_bytes);"),
     "a2a_not_transposed": ("const size_t to = ((size_t)j * (size_t)grid + (size_t)i) * block_bytes;",
                            "const size_t to = from;"),
+    "reduce_drops_last_rank": ("for (int r = 1; r < world; ++r) {", "for (int r = 1; r < world - 1; ++r) {"),
+    "reduce_starts_from_plus_zero": ("float acc = f32_from_bf16(in[0][e]);",
+                                     "float acc = 0.0f + f32_from_bf16(in[0][e]);"),
+    "reduce_reverse_order": ("acc = acc + f32_from_bf16(in[r][e]);",
+                             "acc = f32_from_bf16(in[world - 1 - r][e]) + acc;"),
+    "allreduce_wrong_slot": ("const uint16_t* from = (i == rank) ? reduced : peers[i];",
+                             "const uint16_t* from = (i == 0) ? reduced : peers[i];"),
 }
 
 
@@ -63,6 +70,26 @@ def _pins_pass() -> bool:
                 want[(j * 3 + i) * 2:(j * 3 + i) * 2 + 2] = src[(i * 3 + j) * 2:(i * 3 + j) * 2 + 2]
         if not np.array_equal(oracle.all2all_block(src, 3, 2), want):
             return False
+        # reduce-scatter: hand-worked cases and exact integer sums
+        for contribs, want in (([[0x3F80], [0x4B80], [0xCB80]], 0x0000),
+                               ([[0x3F80], [0x3B80], [0x3B80]], 0x3F81),
+                               ([[0x8000], [0x8000], [0x8000]], 0x8000)):
+            got = oracle.reduce_sum_bf16([np.array(c, np.uint16) for c in contribs])
+            if int(got[0]) != want:
+                return False
+        ints = np.random.default_rng(5).integers(-16, 17, size=(8, 64))
+        enc = [((ints[r].astype(np.float32).view(np.uint32)) >> np.uint32(16)).astype(np.uint16)
+               for r in range(8)]
+        want = (ints.sum(axis=0).astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+        if not np.array_equal(oracle.reduce_sum_bf16(enc), want):
+            return False
+        # all-reduce slot placement (every peer slot holds a real buffer, so a wrong slot reads
+        # valid memory and is caught by the comparison)
+        peers = [np.full(3, 0x1000 + i, np.uint16) for i in range(4)]
+        reduced, dst = oracle.allreduce_local([e[:3].copy() for e in enc[:4]], peers, 2)
+        for i in range(4):
+            if not np.array_equal(dst[i * 3:(i + 1) * 3], reduced if i == 2 else peers[i]):
+                return False
         return True
     except Exception:
         return False
