@@ -30,18 +30,20 @@ C3_MOVER_CU = 0
 C3_MOVER_SDMA = 1
 C3_COPY_GATHER = 0
 C3_COPY_ALL2ALL = 1
+C3_COPY_ALLREDUCE = 2
 C3_FAULT_NONE = 0
 C3_FAULT_DROP_CHUNK = 1
 C3_FAULT_STUCK_CHUNK = 2
 C3_FAULT_ERROR_CHUNK = 3
 C3_MAX_MASK_WORDS = 8
+C3_MAX_WORLD = 64
 TAXONOMY = {0: "GC-equal", 1: "G-long", 2: "C-long"}
 
 # Every symbol include/c3.h declares.
 EXPORTS = ("c3_init", "c3_finalize", "c3_last_error", "c3_device_info", "c3_stream_create",
            "c3_stream_destroy", "c3_cu_mask_balanced", "c3_probe_placement", "c3_gemm",
-           "c3_gather", "c3_all2all_block", "c3_flush_llc", "c3_run_concurrent",
-           "c3_derive_metrics")
+           "c3_gather", "c3_all2all_block", "c3_reduce_scatter", "c3_allreduce_local",
+           "c3_flush_llc", "c3_run_concurrent", "c3_derive_metrics")
 
 
 class C3Error(RuntimeError):
@@ -83,7 +85,9 @@ class c3_copy_args(ctypes.Structure):
                 ("shards", ctypes.POINTER(ctypes.c_void_p)), ("n_shards", ctypes.c_int32),
                 ("grid", ctypes.c_int32), ("shard_bytes", ctypes.c_uint64),
                 ("src", ctypes.c_void_p), ("block_bytes", ctypes.c_uint64),
-                ("opts", c3_move_opts)]
+                ("opts", c3_move_opts), ("peers", ctypes.POINTER(ctypes.c_void_p)),
+                ("reduced", ctypes.c_void_p), ("rank", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class c3_conc_opts(ctypes.Structure):
@@ -99,7 +103,8 @@ class c3_timing(ctypes.Structure):
                 ("gemm_gpu_ms", ctypes.c_double), ("copy_gpu_ms", ctypes.c_double),
                 ("sdma_first_start_ns", ctypes.c_int64), ("sdma_last_end_ns", ctypes.c_int64),
                 ("n_chunks", ctypes.c_int32), ("engines_used", ctypes.c_uint32),
-                ("applied_priority", ctypes.c_int32), ("comm_issued_first", ctypes.c_int32)]
+                ("applied_priority", ctypes.c_int32), ("comm_issued_first", ctypes.c_int32),
+                ("t_reduce_done_ns", ctypes.c_int64), ("reduce_gpu_ms", ctypes.c_double)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -151,6 +156,11 @@ def load(path: Optional[str] = None):
                             ctypes.POINTER(c3_move_opts), vp]
     L.c3_all2all_block.argtypes = [vp, vp, ctypes.c_int, ctypes.c_size_t, ctypes.c_int,
                                    ctypes.POINTER(c3_move_opts), vp]
+    L.c3_reduce_scatter.argtypes = [vp, ctypes.POINTER(vp), ctypes.c_int, ctypes.c_size_t,
+                                    ctypes.POINTER(c3_move_opts), vp]
+    L.c3_allreduce_local.argtypes = [vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_size_t, ctypes.c_int,
+                                     ctypes.POINTER(c3_move_opts), vp]
     L.c3_flush_llc.argtypes = [ctypes.c_size_t, vp]
     L.c3_run_concurrent.argtypes = [ctypes.POINTER(c3_gemm_args), ctypes.POINTER(c3_copy_args),
                                     ctypes.POINTER(c3_conc_opts), ctypes.POINTER(c3_timing)]
@@ -263,6 +273,25 @@ def c3_all2all_block(dst, src, grid: int, block_bytes: int, mover: int = C3_MOVE
                                   _stream(stream)))
 
 
+def _ptr_array(xs):
+    return (ctypes.c_void_p * max(1, len(xs)))(*[_ptr(x) for x in xs])
+
+
+def c3_reduce_scatter(out, contribs, chunk_bytes: int, opts=None, stream=None) -> None:
+    o = ctypes.byref(opts) if opts is not None else None
+    check(load().c3_reduce_scatter(_ptr(out), _ptr_array(contribs), len(contribs), chunk_bytes, o,
+                                   _stream(stream)))
+
+
+def c3_allreduce_local(dst, reduced, contribs, peers, rank: int, chunk_bytes: int,
+                       mover: int = C3_MOVER_CU, opts=None, stream=None) -> None:
+    """peers[i] is rank i's reduced chunk for i != rank (peers[rank] may be None)."""
+    o = ctypes.byref(opts) if opts is not None else None
+    check(load().c3_allreduce_local(_ptr(dst), _ptr(reduced), _ptr_array(contribs),
+                                    _ptr_array(peers), len(contribs), rank, chunk_bytes, mover, o,
+                                    _stream(stream)))
+
+
 def c3_flush_llc(nbytes: int, stream=None) -> None:
     check(load().c3_flush_llc(nbytes, _stream(stream)))
 
@@ -297,6 +326,25 @@ def all2all_args(dst, src, grid, block_bytes, mover, opts=None):
     if opts is not None:
         a.opts = opts
     return a, None
+
+
+def allreduce_args(dst, reduced, contribs, peers, rank, chunk_bytes, mover, opts=None):
+    """A c3_copy_args for an all-reduce local share; the returned tuple keeps the pointer arrays
+    alive."""
+    cp, pp = _ptr_array(contribs), _ptr_array(peers)
+    a = c3_copy_args()
+    a.kind = C3_COPY_ALLREDUCE
+    a.mover = mover
+    a.dst = _ptr(dst)
+    a.shards = ctypes.cast(cp, ctypes.POINTER(ctypes.c_void_p))
+    a.n_shards = len(contribs)
+    a.shard_bytes = chunk_bytes
+    a.peers = ctypes.cast(pp, ctypes.POINTER(ctypes.c_void_p))
+    a.reduced = _ptr(reduced)
+    a.rank = rank
+    if opts is not None:
+        a.opts = opts
+    return a, (cp, pp)
 
 
 def conc_opts(gemm_mask=None, comm_mask=None, comm_first=False, flush_bytes=0,

@@ -19,8 +19,32 @@ c3_status ensure_flush_buffer(size_t bytes);
 c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_conc_opts* o,
                          c3_timing* t);
 
-c3_status copy_segments(const c3_copy_args& a, std::vector<Segment>* segs, size_t* dst_bytes) {
-    segs->clear();
+// Validate a reduce-scatter local share: world contributions of chunk_bytes (bf16) into out.
+c3_status reduce_args(void* out, const void* const* contribs, int world, size_t chunk_bytes,
+                      ReduceArgs* r) {
+    if (world < 1 || world > kMaxWorld)
+        return fail(C3_E_INVALID, "reduce-scatter: world must be in [1, %d]", kMaxWorld);
+    if (chunk_bytes % 2) return fail(C3_E_INVALID, "reduce-scatter: chunk_bytes must be even (bf16)");
+    if (!contribs) return fail(C3_E_INVALID, "reduce-scatter: contributions array is NULL");
+    if (!out) return fail(C3_E_INVALID, "reduce-scatter: output is NULL");
+    r->world = world;
+    r->out = out;
+    r->elems = chunk_bytes / 2;
+    if (chunk_bytes == 0) return C3_OK;
+    C3_TRY(check_device_ptr(out, chunk_bytes, "reduce-scatter output"));
+    for (int i = 0; i < world; ++i) {
+        C3_TRY(check_device_ptr(contribs[i], chunk_bytes, "reduce-scatter contribution"));
+        if (ranges_overlap(contribs[i], chunk_bytes, out, chunk_bytes))
+            return fail(C3_E_OVERLAP, "reduce-scatter: contribution %d overlaps the output", i);
+        r->in[i] = contribs[i];
+    }
+    return C3_OK;
+}
+
+c3_status comm_plan(const c3_copy_args& a, CommPlan* plan) {
+    plan->has_reduce = false;
+    plan->segs.clear();
+    std::vector<Segment>* segs = &plan->segs;
     if (!a.dst) return fail(C3_E_INVALID, "copy: dst is NULL");
     if (a.kind == C3_COPY_GATHER) {
         if (a.n_shards < 0 || a.n_shards > C3_MAX_SEGMENTS)
@@ -29,7 +53,6 @@ c3_status copy_segments(const c3_copy_args& a, std::vector<Segment>* segs, size_
         if (a.shard_bytes && (uint64_t)a.n_shards > std::numeric_limits<uint64_t>::max() / a.shard_bytes)
             return fail(C3_E_INVALID, "gather: size overflow");
         const size_t total = (size_t)a.n_shards * a.shard_bytes;
-        *dst_bytes = total;
         if (total == 0) return C3_OK;
         C3_TRY(check_device_ptr(a.dst, total, "gather dst"));
         for (int i = 0; i < a.n_shards; ++i) {
@@ -49,7 +72,6 @@ c3_status copy_segments(const c3_copy_args& a, std::vector<Segment>* segs, size_
         if (a.block_bytes && nb > std::numeric_limits<uint64_t>::max() / a.block_bytes)
             return fail(C3_E_INVALID, "all2all: size overflow");
         const size_t total = (size_t)(nb * a.block_bytes);
-        *dst_bytes = total;
         if (total == 0) return C3_OK;
         C3_TRY(check_device_ptr(a.src, total, "all2all src"));
         C3_TRY(check_device_ptr(a.dst, total, "all2all dst"));
@@ -64,20 +86,55 @@ c3_status copy_segments(const c3_copy_args& a, std::vector<Segment>* segs, size_
             }
         return C3_OK;
     }
+    if (a.kind == C3_COPY_ALLREDUCE) {
+        const int world = a.n_shards;
+        const size_t chunk = a.shard_bytes;
+        C3_TRY(reduce_args(a.reduced, a.shards, world, chunk, &plan->reduce));
+        if (a.rank < 0 || a.rank >= world)
+            return fail(C3_E_INVALID, "all-reduce: rank must be in [0, world)");
+        if (world > 1 && !a.peers) return fail(C3_E_INVALID, "all-reduce: peers array is NULL");
+        if (chunk == 0) return C3_OK;
+        if (chunk > (std::numeric_limits<size_t>::max() >> 7))  // world <= 64 = 2^6
+            return fail(C3_E_INVALID, "all-reduce: size overflow");
+        const size_t total = (size_t)world * chunk;
+        C3_TRY(check_device_ptr(a.dst, total, "all-reduce dst"));
+        if (ranges_overlap(a.reduced, chunk, a.dst, total))
+            return fail(C3_E_OVERLAP, "all-reduce: reduced chunk overlaps dst");
+        for (int i = 0; i < world; ++i)
+            if (ranges_overlap(a.shards[i], chunk, a.dst, total))
+                return fail(C3_E_OVERLAP, "all-reduce: contribution %d overlaps dst", i);
+        for (int i = 0; i < world; ++i) {
+            const void* src = a.reduced;
+            if (i != a.rank) {
+                C3_TRY(check_device_ptr(a.peers[i], chunk, "all-reduce peer chunk"));
+                if (ranges_overlap(a.peers[i], chunk, a.dst, total))
+                    return fail(C3_E_OVERLAP, "all-reduce: peer chunk %d overlaps dst", i);
+                if (ranges_overlap(a.peers[i], chunk, a.reduced, chunk))
+                    return fail(C3_E_OVERLAP, "all-reduce: peer chunk %d overlaps the reduced chunk", i);
+                src = a.peers[i];
+            }
+            segs->push_back({src, static_cast<char*>(a.dst) + (size_t)i * chunk, chunk});
+        }
+        plan->has_reduce = true;
+        return C3_OK;
+    }
     return fail(C3_E_INVALID, "copy: unknown kind %d", a.kind);
 }
 
-// Isolated copy on `stream`: CU mover enqueues; SDMA mover drains the stream, issues, waits.
+// Isolated collective on `stream`: the reduce-scatter (if any) and a CU-mover copy are
+// enqueued; with the SDMA mover the stream is drained first, then the transfers are issued and
+// waited for.
 c3_status copy_isolated(const c3_copy_args& a, hipStream_t stream) {
-    std::vector<Segment> segs;
-    size_t dst_bytes = 0;
-    C3_TRY(copy_segments(a, &segs, &dst_bytes));
-    if (segs.empty()) return C3_OK;
-    if (a.mover == C3_MOVER_CU) return copy_cu_enqueue(segs, a.opts, stream);
-    if (a.mover != C3_MOVER_SDMA) return fail(C3_E_INVALID, "unknown mover %d", a.mover);
+    CommPlan plan;
+    C3_TRY(comm_plan(a, &plan));
+    if (a.mover != C3_MOVER_CU && a.mover != C3_MOVER_SDMA)
+        return fail(C3_E_INVALID, "unknown mover %d", a.mover);
+    if (plan.has_reduce) C3_TRY(reduce_enqueue(plan.reduce, stream));
+    if (plan.segs.empty()) return C3_OK;
+    if (a.mover == C3_MOVER_CU) return copy_cu_enqueue(plan.segs, a.opts, stream);
     C3_HIP_TRY(hipStreamSynchronize(stream));
     SdmaOp op;
-    C3_TRY(sdma_issue(segs, a.opts, &op));
+    C3_TRY(sdma_issue(plan.segs, a.opts, &op));
     c3_timing t{};
     return sdma_finish(&op, &t);
 }
@@ -209,6 +266,37 @@ c3_status c3_all2all_block(void* dst, const void* src, int grid, size_t block_by
         a.src = src;
         a.grid = grid;
         a.block_bytes = block_bytes;
+        if (opt) a.opts = *opt;
+        return copy_isolated(a, static_cast<hipStream_t>(stream));
+    })
+}
+
+c3_status c3_reduce_scatter(void* out, const void* const* contribs, int world, size_t chunk_bytes,
+                            const c3_move_opts* opt, void* stream) {
+    (void)opt;
+    C3_ENTRY({
+        C3_TRY(require_init());
+        ReduceArgs r;
+        C3_TRY(reduce_args(out, contribs, world, chunk_bytes, &r));
+        return reduce_enqueue(r, static_cast<hipStream_t>(stream));
+    })
+}
+
+c3_status c3_allreduce_local(void* dst, void* reduced, const void* const* contribs,
+                             const void* const* peers, int world, int rank, size_t chunk_bytes,
+                             c3_mover ag_mover, const c3_move_opts* opt, void* stream) {
+    C3_ENTRY({
+        C3_TRY(require_init());
+        c3_copy_args a{};
+        a.kind = C3_COPY_ALLREDUCE;
+        a.mover = ag_mover;
+        a.dst = dst;
+        a.shards = contribs;
+        a.n_shards = world;
+        a.shard_bytes = chunk_bytes;
+        a.peers = peers;
+        a.reduced = reduced;
+        a.rank = rank;
         if (opt) a.opts = *opt;
         return copy_isolated(a, static_cast<hipStream_t>(stream));
     })

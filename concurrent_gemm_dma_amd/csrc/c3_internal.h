@@ -5,6 +5,7 @@
 #include <hsa/hsa.h>
 #include <hsa/hsa_ext_amd.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <mutex>
 #include <string>
@@ -91,6 +92,26 @@ c3_status copy_cu_enqueue(const std::vector<Segment>& segs, const c3_move_opts& 
                           hipStream_t stream);
 c3_status flush_enqueue(void* buf, size_t bytes, hipStream_t stream);
 c3_status probe_enqueue(int n_blocks, uint32_t* out_dev, hipStream_t stream);
+
+// ---- reduce-scatter (reduce.hip) ------------------------------------------------------------------
+constexpr int kMaxWorld = C3_MAX_WORLD;
+struct ReduceArgs {
+    const void* in[kMaxWorld] = {};
+    int world = 0;
+    void* out = nullptr;
+    uint64_t elems = 0;  // bf16 elements per rank
+};
+// Launch only: out[e] = bf16(fp32 sum of in[0..world-1][e] in rank order).
+c3_status reduce_enqueue(const ReduceArgs& a, hipStream_t stream);
+
+// A collective's local share as launched: optional reduce-scatter, then copy segments.
+struct CommPlan {
+    bool has_reduce = false;
+    ReduceArgs reduce;
+    std::vector<Segment> segs;
+};
+// Validate a c3_copy_args and turn it into a plan (no launch, no allocation on the device).
+c3_status comm_plan(const c3_copy_args& a, CommPlan* plan);
 
 // ---- SDMA (sdma.cpp) ----------------------------------------------------------------------------
 c3_status sdma_discover();

@@ -12,6 +12,10 @@
 //   default priority.
 // * Completion: the host polls the GEMM's end event and the copy's end event (CU mover) or
 //   completion signals (SDMA mover) and timestamps each completion on a monotonic clock.
+// * All-reduce (reduce-scatter + all-gather; L3 Synthesis page on 2412.14335, section 3,
+//   Attack 1): the reduce-scatter kernel runs on the communication stream whatever the mover;
+//   a CU-mover all-gather follows it on that stream, an SDMA all-gather is issued by the
+//   polling loop as soon as the reduce-scatter's end event has completed.
 #include <algorithm>
 #include <array>
 #include <chrono>
@@ -44,7 +48,7 @@ std::set<hipStream_t>& user_streams() {
 }
 
 struct Events {
-    hipEvent_t g0 = nullptr, g1 = nullptr, c0 = nullptr, c1 = nullptr;
+    hipEvent_t g0 = nullptr, g1 = nullptr, c0 = nullptr, c1 = nullptr, r1 = nullptr;
 };
 Events& events() {
     static Events e;
@@ -87,6 +91,7 @@ c3_status ensure_events() {
         C3_HIP_TRY(hipEventCreate(&e.g1));
         C3_HIP_TRY(hipEventCreate(&e.c0));
         C3_HIP_TRY(hipEventCreate(&e.c1));
+        C3_HIP_TRY(hipEventCreate(&e.r1));
     }
     return C3_OK;
 }
@@ -137,7 +142,7 @@ void release_streams() {
     for (hipStream_t s : user_streams()) (void)hipStreamDestroy(s);
     user_streams().clear();
     Events& e = events();
-    for (hipEvent_t* ev : {&e.g0, &e.g1, &e.c0, &e.c1})
+    for (hipEvent_t* ev : {&e.g0, &e.g1, &e.c0, &e.c1, &e.r1})
         if (*ev) {
             (void)hipEventDestroy(*ev);
             *ev = nullptr;
@@ -154,9 +159,6 @@ c3_status ensure_flush_buffer(size_t bytes) {
     c.flush_bytes = bytes;
     return C3_OK;
 }
-
-// Defined in abi.cpp: validate a copy description and turn it into segments.
-c3_status copy_segments(const c3_copy_args& a, std::vector<Segment>* segs, size_t* dst_bytes);
 
 c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_conc_opts* o_in,
                          c3_timing* t_out) {
@@ -175,29 +177,34 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
         C3_TRY(stream_for_role(0, o.gemm_cu_mask, &gs));
         C3_TRY(gemm_plan(g->A, g->B, g->C, g->M, g->N, g->K, gs, &plan));
     }
-    std::vector<Segment> segs;
+    CommPlan cp;
+    const std::vector<Segment>& segs = cp.segs;
     c3_move_opts mo{};
     bool sdma = false;
     if (c) {
-        size_t dst_bytes = 0;
-        C3_TRY(copy_segments(*c, &segs, &dst_bytes));
+        C3_TRY(comm_plan(*c, &cp));
         mo = c->opts;
         if (c->mover == C3_MOVER_SDMA) {
             sdma = true;
-        } else if (c->mover == C3_MOVER_CU) {
-            C3_TRY(stream_for_role(1, o.comm_cu_mask, &cs));
-        } else {
+        } else if (c->mover != C3_MOVER_CU) {
             return fail(C3_E_INVALID, "unknown mover %d", c->mover);
         }
+        if (!sdma || cp.has_reduce) C3_TRY(stream_for_role(1, o.comm_cu_mask, &cs));
         if (g) {
             const size_t a_b = (size_t)g->M * g->K * 2, b_b = (size_t)g->K * g->N * 2,
                          c_b = (size_t)g->M * g->N * 2;
-            for (const Segment& s : segs) {
-                if (ranges_overlap(s.dst, s.bytes, g->A, a_b) ||
-                    ranges_overlap(s.dst, s.bytes, g->B, b_b) ||
-                    ranges_overlap(s.dst, s.bytes, g->C, c_b) ||
-                    ranges_overlap(s.src, s.bytes, g->C, c_b))
+            auto clash = [&](const void* src, const void* dst, size_t n) {
+                return ranges_overlap(dst, n, g->A, a_b) || ranges_overlap(dst, n, g->B, b_b) ||
+                       ranges_overlap(dst, n, g->C, c_b) || ranges_overlap(src, n, g->C, c_b);
+            };
+            for (const Segment& s : segs)
+                if (clash(s.src, s.dst, s.bytes))
                     return fail(C3_E_OVERLAP, "copy buffers overlap the GEMM's operands");
+            if (cp.has_reduce) {
+                const size_t n = cp.reduce.elems * 2;
+                for (int r = 0; r < cp.reduce.world; ++r)
+                    if (clash(cp.reduce.in[r], cp.reduce.out, n))
+                        return fail(C3_E_OVERLAP, "reduce-scatter buffers overlap the GEMM's operands");
             }
         }
     }
@@ -216,6 +223,8 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
     SdmaOp op;
     c3_status gemm_st = C3_OK, copy_st = C3_OK;
     bool copy_issued = false, gemm_issued = false;
+    // all-reduce with the SDMA mover: the transfers wait for the reduce-scatter (host-observed)
+    bool reduce_issued = false, sdma_pending = false;
     auto issue_gemm = [&]() {
         if (hipEventRecord(ev.g0, gs) != hipSuccess) {
             gemm_st = fail(C3_E_HIP, "hipEventRecord failed");
@@ -227,7 +236,24 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
         gemm_issued = gemm_st == C3_OK;
     };
     auto issue_copy = [&]() {
-        if (sdma) {
+        if (cp.has_reduce) {
+            if (hipEventRecord(ev.c0, cs) != hipSuccess) {
+                copy_st = fail(C3_E_HIP, "hipEventRecord failed");
+                return;
+            }
+            copy_st = reduce_enqueue(cp.reduce, cs);
+            if (copy_st == C3_OK && hipEventRecord(ev.r1, cs) != hipSuccess)
+                copy_st = fail(C3_E_HIP, "hipEventRecord failed");
+            if (copy_st != C3_OK) return;
+            reduce_issued = true;
+            if (sdma) {
+                sdma_pending = true;  // issued from the polling loop
+            } else {
+                copy_st = copy_cu_enqueue(segs, mo, cs);
+                if (copy_st == C3_OK && hipEventRecord(ev.c1, cs) != hipSuccess)
+                    copy_st = fail(C3_E_HIP, "hipEventRecord failed");
+            }
+        } else if (sdma) {
             copy_st = sdma_issue(segs, mo, &op);
         } else {
             if (hipEventRecord(ev.c0, cs) != hipSuccess) {
@@ -249,7 +275,14 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
 
     // ---- poll for completion ----
     bool gdone = !gemm_issued, cdone = !copy_issued;
-    int64_t tg = 0, tc = 0;
+    bool sdma_issued = sdma && copy_issued && !cp.has_reduce;
+    bool reduce_seen = !reduce_issued;
+    int64_t tg = 0, tc = 0, tr = 0;
+    if (reduce_issued && !copy_issued) {
+        // the reduce-scatter was launched but the step after it failed to launch
+        (void)hipEventSynchronize(ev.r1);
+        reduce_seen = true;
+    }
     while (!(gdone && cdone)) {
         if (!gdone) {
             const hipError_t e = hipEventQuery(ev.g1);
@@ -261,7 +294,29 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
                 gdone = true;
             }
         }
-        if (!cdone) {
+        if (!reduce_seen) {
+            const hipError_t e = hipEventQuery(ev.r1);
+            if (e == hipSuccess) {
+                reduce_seen = true;
+                tr = now_ns() - t0;
+                if (sdma_pending) {
+                    // all-gather on the engines: issued once the reduced chunk exists
+                    sdma_pending = false;
+                    copy_st = sdma_issue(segs, mo, &op);
+                    if (copy_st == C3_OK) sdma_issued = true;
+                    else cdone = true;
+                }
+            } else if (e != hipErrorNotReady) {
+                copy_st = fail(C3_E_HIP, "reduce-scatter completion query failed: %s",
+                               hipGetErrorString(e));
+                reduce_seen = true;
+                if (sdma_pending) {
+                    sdma_pending = false;
+                    cdone = true;
+                }
+            }
+        }
+        if (!cdone && !sdma_pending) {
             if (sdma) {
                 if (sdma_done(op)) {
                     cdone = true;
@@ -284,13 +339,20 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
     const int64_t t1 = now_ns();
 
     c3_timing t{};
-    if (sdma && copy_issued) {
+    if (sdma_issued) {
         const c3_status st = sdma_finish(&op, &t);
         if (st != C3_OK) copy_st = st;
     }
     // Make sure nothing is still running before returning (errors included).
     if (gemm_issued) (void)hipEventSynchronize(ev.g1);
     if (copy_issued && !sdma) (void)hipEventSynchronize(ev.c1);
+    if (reduce_issued) {
+        (void)hipEventSynchronize(ev.r1);
+        if (!tr) tr = now_ns() - t0;  // first observed here (the copy finished before a poll saw it)
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, ev.c0, ev.r1) == hipSuccess) t.reduce_gpu_ms = ms;
+        t.t_reduce_done_ns = tr;
+    }
 
     t.t_conc_ns = t1 - t0;
     t.t_gemm_done_ns = tg;
@@ -306,6 +368,10 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
         float ms = 0.f;
         if (hipEventElapsedTime(&ms, ev.c0, ev.c1) == hipSuccess) t.copy_gpu_ms = ms;
         t.n_chunks = (int32_t)segs.size();
+    }
+    if (sdma_issued && cp.has_reduce) {
+        // the engines' span covers the all-gather only; add the reduce-scatter's kernel time
+        t.copy_gpu_ms += t.reduce_gpu_ms;
     }
     if (t_out) *t_out = t;
     if (gemm_st != C3_OK) return gemm_st;

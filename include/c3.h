@@ -37,9 +37,10 @@
 extern "C" {
 #endif
 
-#define C3_ABI_VERSION 1
+#define C3_ABI_VERSION 2
 #define C3_MAX_MASK_WORDS 8 /* CU masks cover up to 256 CUs, bit i = CU i as the driver numbers it */
 #define C3_MAX_SEGMENTS 4096
+#define C3_MAX_WORLD 64 /* ranks of a reduce-scatter / all-reduce local share */
 
 typedef enum {
     C3_OK = 0,
@@ -54,7 +55,7 @@ typedef enum {
 } c3_status;
 
 typedef enum { C3_MOVER_CU = 0, C3_MOVER_SDMA = 1 } c3_mover;
-typedef enum { C3_COPY_GATHER = 0, C3_COPY_ALL2ALL = 1 } c3_copy_kind;
+typedef enum { C3_COPY_GATHER = 0, C3_COPY_ALL2ALL = 1, C3_COPY_ALLREDUCE = 2 } c3_copy_kind;
 
 /* Test hooks for the SDMA mover, all forced from the host (no GPU fault is ever provoked):
  * DROP  - chunk `fault_chunk` is not issued and its completion is faked: the destination keeps
@@ -100,7 +101,7 @@ typedef struct {
                               0 = every engine available for device-local copies). Chunk c goes
                               to the (c mod n)-th engine of the mask. */
     int32_t nontemporal;   /* CU: 1 = streaming (non-temporal) loads and stores */
-    int32_t cu_blocks;     /* CU: workgroups to launch (0 = one per 64 KiB of payload) */
+    int32_t cu_blocks;     /* CU: workgroups to launch (0 = one per 8 KiB of payload) */
     int32_t timeout_ms;    /* SDMA: wait limit per call (0 = 20000 ms) */
     int32_t fault_mode;    /* c3_fault test hook (0 = off) */
     int32_t fault_chunk;   /* chunk index the fault hook applies to */
@@ -115,25 +116,34 @@ typedef struct {
     int64_t M, N, K;
 } c3_gemm_args;
 
-/* One collective-shaped copy (see c3_gather and c3_all2all_block for the layouts). */
+/* One collective's local share (see c3_gather, c3_all2all_block and c3_allreduce_local for the
+ * layouts). For C3_COPY_ALLREDUCE, `mover` moves the all-gather half; the reduce-scatter half
+ * always runs on the compute units. */
 typedef struct {
     int32_t kind;               /* c3_copy_kind */
     int32_t mover;              /* c3_mover */
     void* dst;
-    const void* const* shards;  /* gather: host array of n_shards device pointers */
+    const void* const* shards;  /* gather: host array of n_shards device pointers;
+                                   all-reduce: the n_shards (= world) ranks' contributions */
     int32_t n_shards;
     int32_t grid;               /* all-to-all: grid x grid blocks */
-    uint64_t shard_bytes;       /* gather: bytes per shard */
+    uint64_t shard_bytes;       /* gather: bytes per shard; all-reduce: bytes per chunk */
     const void* src;            /* all-to-all: source holding grid*grid blocks */
     uint64_t block_bytes;       /* all-to-all: bytes per block */
     c3_move_opts opts;
+    const void* const* peers;   /* all-reduce: host array of world device pointers, the other
+                                   ranks' reduced chunks (entry `rank` is not read) */
+    void* reduced;              /* all-reduce: this rank's reduced chunk (shard_bytes) */
+    int32_t rank;               /* all-reduce: slot of `reduced` in dst */
+    int32_t reserved;
 } c3_copy_args;
 
 /* Controls of one concurrent run. Zero-initialised means: all CUs for both, GEMM issued first,
  * no flush. */
 typedef struct {
     uint32_t gemm_cu_mask[C3_MAX_MASK_WORDS]; /* all zero = every CU */
-    uint32_t comm_cu_mask[C3_MAX_MASK_WORDS]; /* all zero = every CU (CU mover only) */
+    uint32_t comm_cu_mask[C3_MAX_MASK_WORDS]; /* all zero = every CU (CU-mover copies and any
+                                                 reduce-scatter) */
     int32_t comm_first;   /* 1 = issue the communication before the GEMM */
     int32_t use_priority; /* must be 0: every stream stays at default priority; the
                              prioritization control is the issue order (comm_first) */
@@ -151,13 +161,16 @@ typedef struct {
     int64_t t_issue_ns;      /* time spent issuing both operations */
     double gemm_gpu_ms;      /* HIP events around the GEMM launch(es) */
     double copy_gpu_ms;      /* CU mover: HIP events; SDMA: last end - first start of the
-                                engines' own copy timestamps */
+                                engines' own copy timestamps (all-reduce: plus the
+                                reduce-scatter's kernel time) */
     int64_t sdma_first_start_ns; /* SDMA timestamps relative to the earliest chunk start */
     int64_t sdma_last_end_ns;
     int32_t n_chunks;        /* transfers issued (SDMA) or segments copied (CU) */
     uint32_t engines_used;   /* SDMA engines that received a chunk */
     int32_t applied_priority;/* always 0 (default priority) */
     int32_t comm_issued_first;
+    int64_t t_reduce_done_ns;/* all-reduce: first issue -> reduce-scatter completion observed */
+    double reduce_gpu_ms;    /* all-reduce: HIP events around the reduce-scatter kernel(s) */
 } c3_timing;
 
 /* Derived metrics of one concurrent run (abstract; Section IV-B3, Fig. 7). */
@@ -247,6 +260,31 @@ c3_status c3_gather(void* dst, const void* const* shards, int n_shards, size_t s
 c3_status c3_all2all_block(void* dst, const void* src, int grid, size_t block_bytes,
                            c3_mover mover, const c3_move_opts* opt, void* stream);
 
+/* Reduce-scatter local share on the compute units: out[e] = sum over r < world of
+ * contribs[r][e], bf16 elements, e < chunk_bytes / 2. The sum is accumulated in fp32 starting
+ * from rank 0's value with ranks added in order, then rounded once to nearest-even bf16 (a NaN
+ * stays a NaN; its payload is not specified). `contribs` is a host array of world device
+ * pointers; 1 <= world <= C3_MAX_WORLD; chunk_bytes must be even (0 is a no-op); any 2-byte
+ * alignment (16-byte aligned pointers take the vector path). `out` must not overlap any
+ * contribution (C3_E_OVERLAP). Stream-ordered and asynchronous. `opt` is unused (may be NULL).
+ * DMA engines do no arithmetic, so this half of an all-reduce stays on the CUs (L3 Synthesis
+ * page on 2412.14335, section 3, Attack 1; Pith review, Reading between the lines). */
+c3_status c3_reduce_scatter(void* out, const void* const* contribs, int world, size_t chunk_bytes,
+                            const c3_move_opts* opt, void* stream);
+
+/* All-reduce local share = reduce-scatter, then all-gather of the reduced chunks:
+ * reduced = c3_reduce_scatter(contribs); then dst slot i (chunk_bytes each, world slots) receives
+ * `reduced` for i == rank and peers[i] otherwise. `peers` is a host array of world device
+ * pointers (peers[rank] is not read); on one GPU they stand in for the chunks the other ranks
+ * reduced. The all-gather starts only after the reduce-scatter completed and is moved by
+ * `ag_mover`: CU - both halves stream-ordered and asynchronous on `stream`; SDMA - the
+ * reduce-scatter runs on `stream`, the call waits for it, issues the transfers and returns when
+ * they completed. dst and reduced must not overlap each other or any contribution or peer.
+ * (Same passages as c3_reduce_scatter; the all-gather is c3_gather's.) */
+c3_status c3_allreduce_local(void* dst, void* reduced, const void* const* contribs,
+                             const void* const* peers, int world, int rank, size_t chunk_bytes,
+                             c3_mover ag_mover, const c3_move_opts* opt, void* stream);
+
 /* Read `bytes` of a library-owned scratch buffer on `stream`, which evicts the Infinity Cache
  * and leaves it holding clean lines (writes one word per workgroup into the scratch's first
  * 8 KiB). Allocates the scratch on first use or growth; below 32 KiB nothing is done. */
@@ -264,6 +302,9 @@ c3_status c3_flush_llc(size_t bytes, void* stream);
  * communication then the GEMM if o->comm_first, else the GEMM then the communication (the GEMM
  * on a stream masked to o->gemm_cu_mask, a CU-mover copy on a second stream masked to
  * o->comm_cu_mask, an SDMA copy on the engines); poll both for completion; stop the clock.
+ * An all-reduce (c->kind = C3_COPY_ALLREDUCE) runs its reduce-scatter on the o->comm_cu_mask
+ * stream whatever the mover; with the SDMA mover the host issues the all-gather transfers as
+ * soon as it observes the reduce-scatter complete (t_reduce_done_ns).
  * Library streams are created once per distinct mask and reused. Errors of either operation are
  * reported after both have finished. */
 c3_status c3_run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_conc_opts* o,

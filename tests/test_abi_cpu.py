@@ -54,14 +54,41 @@ def test_calls_before_init_are_rejected(c3):
     assert c3.call("c3_device_info", info) == c3.C3_E_NOT_INIT
 
 
+def test_struct_layouts_match_c_compiler(c3, tmp_path):
+    """Every binding struct's size and field offsets equal what a C compiler makes of c3.h."""
+    import ctypes
+    import subprocess
+
+    structs = [c3.c3_info, c3.c3_move_opts, c3.c3_gemm_args, c3.c3_copy_args, c3.c3_conc_opts,
+               c3.c3_timing, c3.c3_metrics]
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "c3.h"', "int main(void) {"]
+    want = []
+    for st in structs:
+        name = st.__name__
+        lines.append(f'printf("%zu\\n", sizeof({name}));')
+        want.append(ctypes.sizeof(st))
+        for fname, _ in st._fields_:
+            lines.append(f'printf("%zu\\n", offsetof({name}, {fname}));')
+            want.append(getattr(st, fname).offset)
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), "-o", str(exe), str(src)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    assert got == want
+
+
 def test_struct_sizes_match_header_layout(c3):
     import ctypes
 
     assert ctypes.sizeof(c3.c3_move_opts) == 40
     assert ctypes.sizeof(c3.c3_gemm_args) == 48
-    assert ctypes.sizeof(c3.c3_copy_args) == 56 + 40
+    assert ctypes.sizeof(c3.c3_copy_args) == 56 + 40 + 24
     assert ctypes.sizeof(c3.c3_conc_opts) == 32 + 32 + 8 + 8
-    assert ctypes.sizeof(c3.c3_timing) == 8 * 8 + 16
+    assert ctypes.sizeof(c3.c3_timing) == 8 * 8 + 16 + 16
     assert ctypes.sizeof(c3.c3_metrics) == 6 * 8 + 8
     assert ctypes.sizeof(c3.c3_info) == 12 * 4 + 8 + 64
 

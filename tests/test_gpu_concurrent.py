@@ -103,10 +103,26 @@ class Case:
         self.dA, self.dB = to_dev(self.A), to_dev(self.B)
         self.dC = empty_bf16((M, N))
         self.copy, self.units, self.unit_bytes = copy, units, unit_bytes
+        self.reduced = None
         if copy == "gather":
             self.src_np = [wl.gen_bytes(unit_bytes, seed + 10 + i) for i in range(units)]
             self.src = [to_dev(s) for s in self.src_np]
             self.want = oracle.gather(self.src_np)
+        elif copy == "allreduce":
+            # units = world, unit_bytes = chunk bytes; this rank is 1
+            n = unit_bytes // 2
+            self.rank = 1
+            self.contribs_np = [wl.gen_bf16((n,), ("normal", 0.0, 1.0), seed + 10 + r)
+                                for r in range(units)]
+            self.peers_np = [None if i == self.rank else
+                             wl.gen_bf16((n,), ("normal", 0.0, 1.0), seed + 100 + i)
+                             for i in range(units)]
+            self.contribs = [to_dev(c) for c in self.contribs_np]
+            self.peers = [None if p is None else to_dev(p) for p in self.peers_np]
+            want_red, want = oracle.allreduce_local(self.contribs_np, self.peers_np, self.rank)
+            self.want_reduced = want_red.view(np.uint8)
+            self.want = want.view(np.uint8)
+            self.reduced = empty_bytes(unit_bytes)
         else:
             self.src_np = wl.gen_bytes(units * units * unit_bytes, seed + 10)
             self.src = to_dev(self.src_np)
@@ -120,12 +136,22 @@ class Case:
     def cargs(self, c3, mover, opts=None):
         if self.copy == "gather":
             return c3.gather_args(self.dst, self.src, self.unit_bytes, mover, opts)
+        if self.copy == "allreduce":
+            return c3.allreduce_args(self.dst, self.reduced, self.contribs, self.peers, self.rank,
+                                     self.unit_bytes, mover, opts)
         return c3.all2all_args(self.dst, self.src, self.units, self.unit_bytes, mover, opts)
 
     def poison(self, rep):
         self.dC.fill_(-1 - rep)
         self.dst.fill_((0xA5 + rep) & 0xFF)
+        if self.reduced is not None:
+            self.reduced.fill_((0x5A + rep) & 0xFF)
         sync()
+
+    def check_comm(self, label):
+        assert oracle.first_diff(self.want, bytes_from_dev(self.dst)) == -1, label
+        if self.reduced is not None:
+            assert oracle.first_diff(self.want_reduced, bytes_from_dev(self.reduced)) == -1, label
 
 
 def run_cells(c3, case, cells):
@@ -146,7 +172,7 @@ def run_cells(c3, case, cells):
         t = c3.c3_run_concurrent(case.gargs(c3), cargs,
                                  c3.conc_opts(gemm_mask=gm, comm_mask=cm, comm_first=comm_first))
         label = f"cell {mover}/{keep}/{'comm-first' if comm_first else 'gemm-first'}"
-        assert oracle.first_diff(case.want, bytes_from_dev(case.dst)) == -1, label
+        case.check_comm(label)
         got_c = bf16_from_dev(case.dC)
         np.testing.assert_array_equal(got_c, iso_c, err_msg=label)
         assert t["t_conc_ns"] > 0 and t["t_conc_ns"] >= max(t["t_gemm_done_ns"], t["t_copy_done_ns"])
@@ -154,6 +180,12 @@ def run_cells(c3, case, cells):
         assert t["applied_priority"] == 0
         if mover == "sdma":
             assert t["engines_used"] != 0 and t["n_chunks"] >= 1
+        if case.copy == "allreduce":
+            assert t["reduce_gpu_ms"] > 0 and 0 < t["t_reduce_done_ns"] <= t["t_conc_ns"]
+            if mover == "sdma":
+                # the engines' all-gather is issued after the reduce-scatter was seen complete
+                assert t["t_copy_done_ns"] >= t["t_reduce_done_ns"]
+                assert t["copy_gpu_ms"] >= t["reduce_gpu_ms"]
         print(label, {k: t[k] for k in ("t_conc_ns", "t_gemm_done_ns", "t_copy_done_ns",
                                         "gemm_gpu_ms", "copy_gpu_ms", "engines_used")}, flush=True)
 
@@ -180,6 +212,24 @@ def test_concurrent_all2all(c3gpu):
 def test_concurrent_skinny_gemm(c3gpu):
     case = Case(c3gpu, 16, 4096, 2048, "gather", 8, 2 * MiB + 16, 9200)
     run_cells(c3gpu, case, [("cu", 32, True), ("sdma", 32, True), ("sdma", 28, False)])
+
+
+def test_concurrent_allreduce(c3gpu):
+    """All-reduce local share (8 ranks x 1 MiB chunk): reduce-scatter on CUs + all-gather by
+    either mover, concurrent with a GEMM, every mask / order cell."""
+    case = Case(c3gpu, 512, 768, 1024, "allreduce", 8, MiB, 9500)
+    run_cells(c3gpu, case, all_cells(c3gpu))
+
+
+def test_concurrent_allreduce_isolated_and_skinny(c3gpu):
+    case = Case(c3gpu, 16, 2048, 1024, "allreduce", 8, 2 * MiB + 6, 9600)
+    run_cells(c3gpu, case, [("cu", 32, True), ("sdma", 32, True), ("sdma", 28, False)])
+    for mover in (c3gpu.C3_MOVER_CU, c3gpu.C3_MOVER_SDMA):
+        case.poison(7)
+        cargs, _keep = case.cargs(c3gpu, mover)
+        t = c3gpu.c3_run_concurrent(None, cargs, c3gpu.conc_opts(flush_bytes=64 * MiB))
+        case.check_comm(f"isolated all-reduce, mover {mover}")
+        assert t["t_gemm_done_ns"] == 0 and t["t_copy_done_ns"] > 0 and t["reduce_gpu_ms"] > 0
 
 
 def test_isolated_copy_via_run_concurrent(c3gpu):
