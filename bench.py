@@ -12,6 +12,9 @@ byte for byte with its source on the device (the copy's definition) and C bit fo
 isolated GEMM's C. The CPU oracle runs only in the cpu_baseline leg: it computes a bounded
 sample of C's rows (timed), which are then compared with the GPU's rows (untimed).
 
+`--workload 6` runs the same protocol on the all-reduce workload (reduce-scatter on the CUs,
+all-gather by the mover under test).
+
 Other modes print one JSON line per measured cell:
   --mode movers    isolated copy GB/s vs size, CU mover variants and SDMA engine/chunk counts
   --mode grid      the GC-equal workload's gather-size sweep: mover x GEMM CU mask x order
@@ -68,7 +71,7 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--mode", default="c3", choices=["c3", "movers", "grid", "cus"])
-    p.add_argument("--workload", type=int, default=2, help="workload id (1..5)")
+    p.add_argument("--workload", type=int, default=2, help="workload id (1..6)")
     p.add_argument("--gather-mib", type=int, default=0, help="workload 5: total gather MiB")
     p.add_argument("--keep-per-xcc", type=int, default=0,
                    help="GEMM CU mask: CUs kept per XCC (0 = all)")
@@ -99,8 +102,24 @@ class Setup:
             self.dC = torch.empty((w.M, w.N), dtype=torch.int16, device=dev)
             self.gargs = c3.gemm_args(self.dA, self.dB, self.dC, w.M, w.N, w.K)
         self.iso_c = None
+        self.dred = None
         if w.copy == "gather":
             self.dsrc = [torch.from_numpy(s).to(dev) for s in wl.gen_shards(w)]
+            total = w.units * w.unit_bytes
+        elif w.copy == "allreduce":
+            contribs, peers = wl.gen_allreduce(w)
+            self.rank = wl.ALLREDUCE_RANK
+            self.dsrc = [torch.from_numpy(c.view(np.int16)).to(dev) for c in contribs]
+            self.dpeers = [None if p is None else torch.from_numpy(p.view(np.int16)).to(dev)
+                           for p in peers]
+            self.dred = torch.empty(w.unit_bytes // 2, dtype=torch.int16, device=dev)
+            # the reduced chunk by its definition, with plain torch ops on the device: fp32 sum
+            # in rank order starting from rank 0, one rounding to bf16
+            acc = self.dsrc[0].view(torch.bfloat16).float()
+            for c in self.dsrc[1:]:
+                acc = acc + c.view(torch.bfloat16).float()
+            self.want_red = acc.to(torch.bfloat16).view(torch.int16)
+            del acc
             total = w.units * w.unit_bytes
         else:
             self.dsrc = torch.from_numpy(wl.gen_a2a_source(w)).to(dev)
@@ -114,6 +133,9 @@ class Setup:
         w = self.w
         if w.copy == "gather":
             return self.c3.gather_args(self.ddst, self.dsrc, w.unit_bytes, mover, opts)
+        if w.copy == "allreduce":
+            return self.c3.allreduce_args(self.ddst, self.dred, self.dsrc, self.dpeers, self.rank,
+                                          w.unit_bytes, mover, opts)
         return self.c3.all2all_args(self.ddst, self.dsrc, w.units, w.unit_bytes, mover, opts)
 
     def poison(self):
@@ -121,6 +143,8 @@ class Setup:
         if hasattr(self, "dC"):
             self.dC.fill_(-1 - (self.poison_i % 7))
         self.ddst.fill_((0xA5 + self.poison_i) & 0xFF)
+        if self.dred is not None:
+            self.dred.fill_(-2 - (self.poison_i % 5))
         self.torch.cuda.synchronize()
 
     def verify_copy(self, label):
@@ -133,6 +157,14 @@ class Setup:
             for i, s in enumerate(self.dsrc):
                 if not teq(self.ddst[i * sb:(i + 1) * sb], s):
                     raise SystemExit(f"{label}: gather shard {i} differs from its destination range")
+        elif w.copy == "allreduce":
+            cb = w.unit_bytes
+            if not teq(self.dred, self.want_red):
+                raise SystemExit(f"{label}: reduced chunk differs from the fp32 rank-order sum")
+            for i in range(w.units):
+                src = self.dred if i == self.rank else self.dpeers[i]
+                if not teq(self.ddst[i * cb:(i + 1) * cb], src.view(self.torch.uint8)):
+                    raise SystemExit(f"{label}: all-gather slot {i} differs from its chunk")
         else:
             g, bb = w.units, w.unit_bytes
             for i in range(g):
@@ -189,7 +221,8 @@ def run_c3(args, c3, info):
         w = w.with_gather_total(args.gather_mib * MiB)
     M, N, K = w.M, w.N, w.K
     flops = w.gemm_flops
-    copy_bytes = w.copy_bytes  # payload S; HBM traffic of the copy is 2S (read + write)
+    copy_bytes = w.copy_bytes  # payload S
+    comm_bytes = w.comm_hbm_bytes  # algorithmic HBM bytes of the local share (2S for copies)
     s = Setup(c3, w, check=not args.profile)
 
     gmask = c3.c3_cu_mask_balanced(args.keep_per_xcc) if args.keep_per_xcc else None
@@ -199,7 +232,7 @@ def run_c3(args, c3, info):
     conc = {}
     for name, mv in movers:
         cmask = None
-        if gmask is not None and mv == c3.C3_MOVER_CU:
+        if gmask is not None and (mv == c3.C3_MOVER_CU or w.copy == "allreduce"):
             cmask = c3.c3_cu_mask_balanced(args.keep_per_xcc, complement=True)
         conc[name] = c3.conc_opts(gemm_mask=gmask, comm_mask=cmask, comm_first=comm_first,
                                   flush_bytes=FLUSH_BYTES)
@@ -207,7 +240,7 @@ def run_c3(args, c3, info):
     iso_c_opts = c3.conc_opts(flush_bytes=FLUSH_BYTES)
 
     t_gemm, g_gpu = [], []
-    rec = {name: {"t_copy": [], "c_gpu": [], "t_conc": [], "gk": []} for name, _ in movers}
+    rec = {name: {"t_copy": [], "c_gpu": [], "t_conc": [], "gk": [], "rs": []} for name, _ in movers}
     torch = s.torch
     torch.cuda.synchronize()
     wall0 = time.time()
@@ -231,6 +264,7 @@ def run_c3(args, c3, info):
             if timed:
                 r["t_copy"].append(t["t_conc_ns"] * 1e-9)
                 r["c_gpu"].append(t["copy_gpu_ms"] * 1e-3)
+                r["rs"].append(t["reduce_gpu_ms"] * 1e-3)
             s.poison()
             t = c3.c3_run_concurrent(s.gargs, ca, conc[name])
             s.verify_copy(f"{name} step {i}")
@@ -251,19 +285,23 @@ def run_c3(args, c3, info):
         T_copy = statistics.median(r["t_copy"])
         T_conc = statistics.mean(r["t_conc"])
         c_gpu_med = statistics.median(r["c_gpu"])
-        m = c3.c3_derive_metrics(T_gemm, T_copy, T_conc, float(w.gemm_bytes + 2 * copy_bytes),
+        m = c3.c3_derive_metrics(T_gemm, T_copy, T_conc, float(w.gemm_bytes + comm_bytes),
                                  PEAK_HBM_GBPS * 1e9)
         results[name] = {
             "t_copy_ms": T_copy * 1e3, "t_conc_ms": T_conc * 1e3,
             "t_conc_ms_min": min(r["t_conc"]) * 1e3, "t_conc_ms_max": max(r["t_conc"]) * 1e3,
             "t_conc_ms_std": (statistics.pstdev(r["t_conc"]) * 1e3) if len(r["t_conc"]) > 1 else 0.0,
-            "copy_gbps_isolated": 2 * copy_bytes / T_copy / 1e9,
-            "copy_gbps_isolated_engine_clock": (2 * copy_bytes / c_gpu_med / 1e9
+            "copy_gbps_isolated": comm_bytes / T_copy / 1e9,
+            "copy_gbps_isolated_engine_clock": (comm_bytes / c_gpu_med / 1e9
                                                 if c_gpu_med > 0 else None),
             "gemm_tflops_concurrent": flops / T_conc / 1e12,
-            "copy_gbps_concurrent": 2 * copy_bytes / T_conc / 1e9,
+            "copy_gbps_concurrent": comm_bytes / T_conc / 1e9,
             "gemm_kernel_ms_concurrent": statistics.mean(r["gk"]) * 1e3,
             "speedup_vs_best_serial": (T_gemm + best_copy) / T_conc,
+            **({"reduce_scatter_ms_isolated": statistics.median(r["rs"]) * 1e3,
+                "reduce_scatter_gbps_isolated": ((w.units + 1) * w.unit_bytes
+                                                 / statistics.median(r["rs"]) / 1e9)}
+               if w.copy == "allreduce" else {}),
             **{k: m[k] for k in ("ideal_speedup", "speedup", "uplift_fraction", "ratio_of_ideal",
                                  "gemm_slowdown", "hbm_ceiling", "taxonomy")},
         }
@@ -313,7 +351,7 @@ def run_c3(args, c3, info):
                         f"{w.unit_bytes / MiB:g} MiB; value = SDMA mover, "
                         f"{'comm-first' if comm_first else 'GEMM-first'}, "
                         f"GEMM CUs {'all' if not gmask else str(args.keep_per_xcc) + '/XCC'}",
-            "M": M, "N": N, "K": K, "copy_bytes": copy_bytes,
+            "M": M, "N": N, "K": K, "copy_bytes": copy_bytes, "comm_hbm_bytes": comm_bytes,
         },
         "copy_gbps_concurrent": round(head["copy_gbps_concurrent"], 1),
         "pct_of_ideal_uplift": round(head["uplift_fraction"] * 100, 2),
@@ -329,7 +367,9 @@ def run_c3(args, c3, info):
                   "first issue to both operations complete (SDMA cell); isolated and concurrent "
                   "runs interleaved per step, each after a poison + 512 MiB read flush",
         "wall_s_timed_rounds": round(wall, 3),
-        "verified": "every run: each copy destination range equal to its source (device compare), "
+        "verified": "every run: each copy destination range equal to its source (device compare; "
+                    "all-reduce: the reduced chunk equal to the fp32 rank-order sum done with "
+                    "torch on the device), "
                     "C bit-identical to the isolated C; isolated C vs the CPU oracle on the "
                     "cpu_baseline rows",
         "gemm_parity_vs_oracle": parity,

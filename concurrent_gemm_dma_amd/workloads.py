@@ -11,7 +11,14 @@ training concurrent with FSDP-style all-gathers or MoE-style all-to-alls (Sectio
 the paper's scenario table itself is not available, so these shapes are synthetic stand-ins).
 
 Seeds: seed = 0xC3000000 + 256 * workload_id + buffer_id, buffer ids A = 1, B = 2, shard i =
-16 + i, all-to-all source = 32; the small-integer variant adds 64.
+16 + i (all-reduce: rank r's contribution = 16 + r), all-to-all source = 32, all-reduce peer
+chunk i = 48 + i; the small-integer variant adds 64.
+
+Workload 6 widens the collective to an all-reduce, split into a reduce-scatter (arithmetic, on
+the CUs) and an all-gather of the reduced chunks (a copy either mover can take), the split the
+pages propose because DMA engines do no arithmetic (L3 Synthesis page on 2412.14335, section 3,
+Attack 1): a 256 MiB bf16 gradient bucket over 8 ranks, as data-parallel training all-reduces
+gradients while the next GEMM runs.
 """
 from __future__ import annotations
 
@@ -26,6 +33,7 @@ BUF_A = 1
 BUF_B = 2
 BUF_SHARD0 = 16
 BUF_A2A_SRC = 32
+BUF_PEER0 = 48
 INT_VARIANT = 64
 
 _CHUNK = 1 << 24  # elements per generation chunk (fixed so the streams never depend on size)
@@ -40,16 +48,26 @@ class Workload:
     K: int
     a_dist: tuple          # ("uniform", lo, hi) or ("normal", mean, std)
     b_dist: tuple
-    copy: str              # "gather" or "all2all"
-    units: int             # gather: number of shards; all2all: grid (grid x grid blocks)
-    unit_bytes: int        # gather: bytes per shard; all2all: bytes per block
+    copy: str              # "gather", "all2all" or "allreduce"
+    units: int             # gather: shards; all2all: grid (grid x grid blocks); allreduce: ranks
+    unit_bytes: int        # gather: bytes per shard; all2all: bytes per block; allreduce: chunk
     payload: str           # "bytes" (uniform random bytes) or "bf16_normal"
     sweep_total_bytes: tuple = ()  # gather totals swept by the GC-equal workload
 
     @property
     def copy_bytes(self) -> int:
-        n = self.units if self.copy == "gather" else self.units * self.units
+        """Bytes the collective delivers: the gathered / transposed / all-reduced buffer."""
+        n = self.units * self.units if self.copy == "all2all" else self.units
         return n * self.unit_bytes
+
+    @property
+    def comm_hbm_bytes(self) -> int:
+        """Algorithmic HBM bytes of the local share: copies read and write every byte once;
+        an all-reduce's reduce-scatter reads `units` chunks and writes one, then its all-gather
+        reads and writes `units` chunks."""
+        if self.copy == "allreduce":
+            return (3 * self.units + 1) * self.unit_bytes
+        return 2 * self.copy_bytes
 
     @property
     def gemm_flops(self) -> int:
@@ -78,7 +96,11 @@ WORKLOADS = {
     5: Workload(5, "gc_equal_sweep", 4096, 16384, 8192, ("normal", 0.0, 1.0),
                 ("normal", 0.0, 0.02), "gather", 8, 32 * MiB, "bytes",
                 sweep_total_bytes=tuple(s * MiB for s in (32, 64, 128, 256, 384, 512, 768, 1024))),
+    6: Workload(6, "dp_allreduce_70b_ffn", 8192, 28672, 8192, ("normal", 0.0, 1.0),
+                ("normal", 0.0, 0.02), "allreduce", 8, 32 * MiB, "bf16_normal"),
 }
+
+ALLREDUCE_RANK = 0  # the local rank of the all-reduce workloads
 
 
 def seed_for(wid: int, buf: int) -> int:
@@ -155,6 +177,20 @@ def gen_shards(w: Workload, shard_bytes: Optional[int] = None):
     """Gather sources: list of `units` arrays of `shard_bytes` bytes each."""
     sb = w.unit_bytes if shard_bytes is None else shard_bytes
     return [gen_payload(w, sb, BUF_SHARD0 + i) for i in range(w.units)]
+
+
+def gen_allreduce(w: Workload, chunk_bytes: Optional[int] = None, rank: int = ALLREDUCE_RANK):
+    """All-reduce inputs as uint16 bf16 arrays: (contributions of the `units` ranks to this
+    rank's chunk, the other ranks' reduced chunks with None at `rank`)."""
+    cb = w.unit_bytes if chunk_bytes is None else chunk_bytes
+    if cb % 2:
+        raise ValueError("all-reduce chunks hold bf16: even byte count")
+    n = cb // 2
+    contribs = [gen_bf16((n,), ("normal", 0.0, 1.0), seed_for(w.wid, BUF_SHARD0 + r))
+                for r in range(w.units)]
+    peers = [None if i == rank else gen_bf16((n,), ("normal", 0.0, 1.0), seed_for(w.wid, BUF_PEER0 + i))
+             for i in range(w.units)]
+    return contribs, peers
 
 
 def gen_a2a_source(w: Workload, block_bytes: Optional[int] = None) -> np.ndarray:

@@ -10,6 +10,11 @@ def test_table_shapes():
     assert (w[2].M, w[2].N, w[2].K, w[2].copy_bytes) == (8192, 28672, 8192, 128 * wl.MiB)
     assert (w[3].M, w[3].N, w[3].K, w[3].copy_bytes) == (16, 28672, 8192, 256 * wl.MiB)
     assert (w[4].M, w[4].N, w[4].K, w[4].copy_bytes) == (8192, 53248, 16384, 512 * wl.MiB)
+    assert (w[6].M, w[6].N, w[6].K, w[6].copy_bytes) == (8192, 28672, 8192, 256 * wl.MiB)
+    # all-reduce local share: reduce-scatter reads 8 chunks, writes 1; all-gather reads and
+    # writes 8 chunks (32 MiB each)
+    assert w[6].comm_hbm_bytes == (8 + 1 + 16) * 32 * wl.MiB
+    assert w[2].comm_hbm_bytes == 2 * w[2].copy_bytes
     assert (w[5].M, w[5].N, w[5].K) == (4096, 16384, 8192)
     assert w[5].sweep_total_bytes[0] == 32 * wl.MiB and w[5].sweep_total_bytes[-1] == wl.MiB * 1024
     assert w[5].with_gather_total(64 * wl.MiB).unit_bytes == 8 * wl.MiB
@@ -49,3 +54,13 @@ def test_sample_indices():
     r, c = wl.sample_indices(10, 20, 30, seed=1, full_rows=(2,), full_cols=(19,))
     assert r.size == 30 + 4 + 20 + 10
     assert r.max() < 10 and c.max() < 20
+
+
+def test_allreduce_generator_is_seeded_and_leaves_rank_slot_empty():
+    w = wl.WORKLOADS[6]
+    c1, p1 = wl.gen_allreduce(w, 4096, rank=2)
+    c2, p2 = wl.gen_allreduce(w, 4096, rank=2)
+    assert len(c1) == 8 and all(x.size == 2048 for x in c1)
+    assert p1[2] is None and all(p is not None for i, p in enumerate(p1) if i != 2)
+    assert all((a == b).all() for a, b in zip(c1, c2))
+    assert not (c1[0] == c1[1]).all()
