@@ -25,6 +25,8 @@ Parity status of each routine (pins are in the CPU test suite):
   checkers            pinned: planted mistakes (dropped chunk, flipped byte, swapped shards)
   (mutants)           mistakes planted in a scratch copy of oracle.c fail the pins above
   metrics             pinned: closed forms (S_ideal in [1, 2], = 2 iff equal times)
+  partition           pinned: hand-worked roofline values and machine balance, hand-worked
+                      predictions with the tie rule, limiting tables, scoring
 """
 from __future__ import annotations
 
