@@ -19,6 +19,8 @@ Other modes print one JSON line per measured cell:
   --mode movers    isolated copy GB/s vs size, CU mover variants and SDMA engine/chunk counts
   --mode grid      the GC-equal workload's gather-size sweep: mover x GEMM CU mask x order
   --mode cus       isolated GEMM time and CU-copy GB/s under balanced CU masks
+  --mode partition CU-partitioning sweep (c3_rp) over 30 GEMM x collective scenarios and the
+                   slowdown-lookup-table heuristic scored against it
 
 Prints ONE JSON line on stdout in the default mode. Progress goes to stderr.
 """
@@ -70,7 +72,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--mode", default="c3", choices=["c3", "movers", "grid", "cus"])
+    p.add_argument("--mode", default="c3", choices=["c3", "movers", "grid", "cus", "partition"])
     p.add_argument("--workload", type=int, default=2, help="workload id (1..6)")
     p.add_argument("--gather-mib", type=int, default=0, help="workload 5: total gather MiB")
     p.add_argument("--keep-per-xcc", type=int, default=0,
@@ -86,7 +88,7 @@ def parse():
 class Setup:
     """Seeded inputs of one workload resident in HBM, plus the per-run checks."""
 
-    def __init__(self, c3, w, with_gemm=True, check=True):
+    def __init__(self, c3, w, with_gemm=True, check=True, with_comm=True):
         import numpy as np
         import torch
 
@@ -103,7 +105,9 @@ class Setup:
             self.gargs = c3.gemm_args(self.dA, self.dB, self.dC, w.M, w.N, w.K)
         self.iso_c = None
         self.dred = None
-        if w.copy == "gather":
+        if not with_comm:
+            self.ddst = torch.empty(0, dtype=torch.uint8, device=dev)
+        elif w.copy == "gather":
             self.dsrc = [torch.from_numpy(s).to(dev) for s in wl.gen_shards(w)]
             total = w.units * w.unit_bytes
         elif w.copy == "allreduce":
@@ -124,7 +128,8 @@ class Setup:
         else:
             self.dsrc = torch.from_numpy(wl.gen_a2a_source(w)).to(dev)
             total = w.units * w.units * w.unit_bytes
-        self.ddst = torch.empty(total, dtype=torch.uint8, device=dev)
+        if with_comm:
+            self.ddst = torch.empty(total, dtype=torch.uint8, device=dev)
         self.poison_i = 0
         torch.cuda.synchronize()
         log(f"{w.name}: inputs resident in HBM in {time.time() - t0:.1f} s")
@@ -521,6 +526,148 @@ def run_cus(args, c3, info):
         del s
 
 
+def run_partition(args, c3, info):
+    """Resource partitioning (c3_rp): the GEMM keeps N - c CUs per XCC and a CU-mover collective
+    gets the other c, for c in powers of two; the best split is the sweep's upper bound. The
+    heuristic predicts the split from a one-time slowdown lookup table (calibration kernels,
+    isolated, under each mask) and isolated times estimated by a 0.70-efficiency roofline (or,
+    second variant, measured), and is scored against the sweep: hit = same split, loss =
+    T_conc(chosen) / T_conc(best) - 1. Every configuration of a table or a scenario is run once
+    per round and rounds repeat, so clock drift hits all of them alike; medians over rounds."""
+    import dataclasses
+
+    from concurrent_gemm_dma_amd import workloads as wl
+
+    per = info["n_cu"] // info["n_xcc"]
+    opts = [c for c in (1, 2, 4, 8, 16) if c < per]
+    reps = max(5, args.steps)
+    eff = 0.70
+    base = wl.WORKLOADS[2]
+    peak_f, peak_b = PEAK_BF16_TFLOPS * 1e12, PEAK_HBM_GBPS * 1e9
+
+    def gemm_w(wid, M, N, K):
+        return dataclasses.replace(base, wid=wid, name=f"gemm_{M}x{N}x{K}", M=M, N=N, K=K)
+
+    def comm_w(wid, kind, units, unit_mib):
+        return dataclasses.replace(base, wid=wid, name=f"{kind}_{units}x{unit_mib}MiB", copy=kind,
+                                   units=units, unit_bytes=int(unit_mib * MiB), payload="bytes")
+
+    def mask(keep):
+        return None if keep == per else c3.c3_cu_mask_balanced(keep)
+
+    def run(g, cm, gkeep=per, ckeep=per):
+        """One verified run: GEMM alone (cm None), collective alone (g None), or both with the
+        GEMM on gkeep CUs per XCC and the collective on the complementary ckeep."""
+        for x in (g, cm):
+            if x is not None:
+                x.poison()
+        ca = cm.cargs(c3.C3_MOVER_CU)[0] if cm is not None else None
+        if g is not None and cm is not None:
+            o = c3.conc_opts(gemm_mask=mask(gkeep),
+                             comm_mask=None if gkeep == per else c3.c3_cu_mask_balanced(gkeep, True),
+                             comm_first=True, flush_bytes=FLUSH_BYTES)
+        else:
+            o = c3.conc_opts(gemm_mask=mask(gkeep), comm_mask=mask(ckeep), flush_bytes=FLUSH_BYTES)
+        t = c3.c3_run_concurrent(g.gargs if g is not None else None, ca, o)
+        if cm is not None:
+            cm.verify_copy("partition run")
+        if g is not None:
+            g.verify_c("partition run")
+        return t["t_conc_ns"] * 1e-9
+
+    def medians(cells):
+        """cells: {key: thunk}; one untimed round, then `reps` rounds of every cell."""
+        out = {k: [] for k in cells}
+        for i in range(reps + 1):
+            for k, f in cells.items():
+                t = f()
+                if i:
+                    out[k].append(t)
+        return {k: statistics.median(v) for k, v in out.items()}
+
+    # ---- one-time lookup table from calibration kernels ----
+    calib_gemm = {"compute": gemm_w(20, 4096, 16384, 8192), "memory": gemm_w(21, 16, 28672, 8192)}
+    calib_comm = {"gather": comm_w(22, "gather", 8, 32), "all2all": comm_w(23, "all2all", 8, 4)}
+    tables = {}
+    for cls, w in calib_gemm.items():
+        g = Setup(c3, w, check=not args.profile, with_comm=False)
+        for _ in range(5):  # clocks up before anything is timed
+            run(g, None)
+        m = medians({k: (lambda k=k: run(g, None, gkeep=k)) for k in [per] + [per - c for c in opts]})
+        tables[("gemm", cls)] = {k: m[k] / m[per] for k in m if k != per}
+        del g
+    for kind, w in calib_comm.items():
+        cm = Setup(c3, w, with_gemm=False, check=not args.profile)
+        m = medians({k: (lambda k=k: run(None, cm, ckeep=k)) for k in [per] + opts})
+        tables[("comm", kind)] = {k: m[k] / m[per] for k in m if k != per}
+        del cm
+    for (role, cls), tab in tables.items():
+        print(json.dumps({"mode": "partition", "table": f"{role}:{cls}",
+                          "slowdown_by_cus_per_xcc": {str(k): round(v, 4) for k, v in sorted(tab.items())}}),
+              flush=True)
+
+    # ---- scenarios: GEMMs x CU-mover collectives ----
+    gemms = [(8192, 28672, 8192), (4096, 16384, 8192), (2048, 28672, 8192), (8192, 8192, 8192),
+             (16, 28672, 8192), (32, 53248, 8192)]
+    comms = [("gather", 8, 8), ("gather", 8, 32), ("gather", 8, 128), ("all2all", 8, 1),
+             ("all2all", 8, 4)]
+    comm_setups = [Setup(c3, comm_w(40 + i, *cdef), with_gemm=False, check=not args.profile)
+                   for i, cdef in enumerate(comms)]
+    hits = {"roofline": 0, "measured": 0}
+    losses = {"roofline": [], "measured": []}
+    gain_rp_over_sp = []
+    n = 0
+    for gi, (M, N, K) in enumerate(gemms):
+        w = gemm_w(30 + gi, M, N, K)
+        g = Setup(c3, w, check=not args.profile, with_comm=False)
+        gcls = "compute" if w.gemm_flops / peak_f >= w.gemm_bytes / peak_b else "memory"
+        for _ in range(3):
+            run(g, None)
+        for cm, (kind, units, unit_mib) in zip(comm_setups, comms):
+            cw = cm.w
+            cells = {"gemm": lambda: run(g, None), "comm": lambda: run(None, cm),
+                     "shared": lambda: run(g, cm)}
+            cells.update({c: (lambda c=c: run(g, cm, gkeep=per - c)) for c in opts})
+            m = medians(cells)
+            T_g, T_c = m["gemm"], m["comm"]
+            measured = {c: m[c] for c in opts}
+            best_c = min(opts, key=lambda c: (measured[c], c))
+            est_g = c3.c3_roofline_time(w.gemm_flops, w.gemm_bytes, peak_f, peak_b, eff)
+            est_c = c3.c3_roofline_time(0.0, cw.comm_hbm_bytes, peak_f, peak_b, eff)
+            picks = {}
+            for variant, (tg, tc) in (("roofline", (est_g, est_c)), ("measured", (T_g, T_c))):
+                chosen, preds = c3.c3_predict_partition(tables[("gemm", gcls)], tables[("comm", kind)],
+                                                        tg, tc, per, opts)
+                hit = chosen == best_c
+                loss = measured[chosen] / measured[best_c] - 1.0
+                hits[variant] += hit
+                losses[variant].append(loss)
+                picks[variant] = {"chosen_cus_per_xcc": chosen, "hit": hit, "loss": round(loss, 5),
+                                  "predicted_ms": [round(p * 1e3, 4) for p in preds]}
+            T_sp = m["shared"]
+            mt = c3.c3_derive_metrics(T_g, T_c, measured[best_c])
+            gain_rp_over_sp.append(T_sp / measured[best_c])
+            n += 1
+            print(json.dumps({
+                "mode": "partition", "scenario": n, "gemm": f"{M}x{N}x{K}", "gemm_class": gcls,
+                "collective": cw.name, "t_gemm_ms": round(T_g * 1e3, 4),
+                "t_comm_ms": round(T_c * 1e3, 4), "taxonomy": mt["taxonomy"],
+                "t_conc_ms_by_comm_cus_per_xcc": {str(c): round(v * 1e3, 4) for c, v in measured.items()},
+                "best_comm_cus_per_xcc": best_c, "t_conc_ms_shared_cus": round(T_sp * 1e3, 4),
+                "speedup_best_split": round((T_g + T_c) / measured[best_c], 4),
+                "speedup_shared_cus": round((T_g + T_c) / T_sp, 4),
+                "heuristic": picks}), flush=True)
+        del g
+    print(json.dumps({
+        "mode": "partition", "summary": True, "scenarios": n, "rounds": reps,
+        "heuristic_roofline_0.70": {"hits": hits["roofline"], "max_loss": round(max(losses["roofline"]), 5),
+                                    "mean_loss": round(statistics.mean(losses["roofline"]), 5)},
+        "heuristic_measured_times": {"hits": hits["measured"], "max_loss": round(max(losses["measured"]), 5),
+                                     "mean_loss": round(statistics.mean(losses["measured"]), 5)},
+        "best_split_vs_shared_cus_geomean": round(statistics.geometric_mean(gain_rp_over_sp), 4),
+        "scenarios_where_best_split_beats_shared": sum(x > 1.0 for x in gain_rp_over_sp)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -536,7 +683,8 @@ def main():
     c3.c3_init(0)
     info = c3.c3_device_info()
     log("device:", info)
-    {"c3": run_c3, "movers": run_movers, "grid": run_grid, "cus": run_cus}[args.mode](args, c3, info)
+    {"c3": run_c3, "movers": run_movers, "grid": run_grid, "cus": run_cus,
+     "partition": run_partition}[args.mode](args, c3, info)
     c3.c3_finalize()
 
 

@@ -37,13 +37,15 @@ C3_FAULT_STUCK_CHUNK = 2
 C3_FAULT_ERROR_CHUNK = 3
 C3_MAX_MASK_WORDS = 8
 C3_MAX_WORLD = 64
+C3_MAX_CURVE = 16
 TAXONOMY = {0: "GC-equal", 1: "G-long", 2: "C-long"}
 
 # Every symbol include/c3.h declares.
 EXPORTS = ("c3_init", "c3_finalize", "c3_last_error", "c3_device_info", "c3_stream_create",
            "c3_stream_destroy", "c3_cu_mask_balanced", "c3_probe_placement", "c3_gemm",
            "c3_gather", "c3_all2all_block", "c3_reduce_scatter", "c3_allreduce_local",
-           "c3_flush_llc", "c3_run_concurrent", "c3_derive_metrics")
+           "c3_flush_llc", "c3_run_concurrent", "c3_derive_metrics", "c3_roofline_time",
+           "c3_predict_partition")
 
 
 class C3Error(RuntimeError):
@@ -125,6 +127,12 @@ class c3_metrics(ctypes.Structure):
 _lib = None
 
 
+class c3_slowdown_curve(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("cus_per_xcc", ctypes.c_int32 * C3_MAX_CURVE),
+                ("slowdown", ctypes.c_double * C3_MAX_CURVE)]
+
+
 def load(path: Optional[str] = None):
     """Open libc3.so (after importing torch so both share one HIP runtime). The path defaults
     to the in-tree build; the C3_LIB environment variable names another build of it."""
@@ -165,6 +173,13 @@ def load(path: Optional[str] = None):
     L.c3_run_concurrent.argtypes = [ctypes.POINTER(c3_gemm_args), ctypes.POINTER(c3_copy_args),
                                     ctypes.POINTER(c3_conc_opts), ctypes.POINTER(c3_timing)]
     L.c3_derive_metrics.argtypes = [ctypes.c_double] * 5 + [ctypes.POINTER(c3_metrics)]
+    L.c3_roofline_time.argtypes = [ctypes.c_double] * 5 + [ctypes.POINTER(ctypes.c_double)]
+    L.c3_predict_partition.argtypes = [ctypes.POINTER(c3_slowdown_curve),
+                                       ctypes.POINTER(c3_slowdown_curve), ctypes.c_double,
+                                       ctypes.c_double, ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_int32), ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_int32),
+                                       ctypes.POINTER(ctypes.c_double)]
     for name in EXPORTS:
         if name != "c3_last_error":
             getattr(L, name).restype = st
@@ -373,3 +388,36 @@ def c3_derive_metrics(t_gemm: float, t_copy: float, t_conc: float, bytes_total: 
     check(load().c3_derive_metrics(t_gemm, t_copy, t_conc, bytes_total, bandwidth,
                                    ctypes.byref(m)))
     return m.as_dict()
+
+
+def slowdown_curve(table) -> c3_slowdown_curve:
+    """A c3_slowdown_curve from {cus_per_xcc: slowdown}."""
+    items = sorted(table.items())
+    if not 1 <= len(items) <= C3_MAX_CURVE:
+        raise ValueError(f"a slowdown curve holds 1..{C3_MAX_CURVE} entries")
+    c = c3_slowdown_curve()
+    c.n = len(items)
+    for i, (k, v) in enumerate(items):
+        c.cus_per_xcc[i] = k
+        c.slowdown[i] = v
+    return c
+
+
+def c3_roofline_time(flops: float, nbytes: float, peak_flops: float, peak_bw: float,
+                     efficiency: float = 0.70) -> float:
+    t = ctypes.c_double()
+    check(load().c3_roofline_time(flops, nbytes, peak_flops, peak_bw, efficiency, ctypes.byref(t)))
+    return t.value
+
+
+def c3_predict_partition(gemm_table, comm_table, t_gemm: float, t_comm: float, cus_per_xcc: int,
+                         options) -> tuple:
+    """(chosen CUs per XCC for the collective, predictions per option) from {k: slowdown}
+    tables."""
+    g, c = slowdown_curve(gemm_table), slowdown_curve(comm_table)
+    opts = (ctypes.c_int32 * len(options))(*options)
+    preds = (ctypes.c_double * len(options))()
+    chosen = ctypes.c_int32()
+    check(load().c3_predict_partition(ctypes.byref(g), ctypes.byref(c), t_gemm, t_comm,
+                                      cus_per_xcc, opts, len(options), ctypes.byref(chosen), preds))
+    return chosen.value, list(preds)

@@ -173,6 +173,17 @@ typedef struct {
     double reduce_gpu_ms;    /* all-reduce: HIP events around the reduce-scatter kernel(s) */
 } c3_timing;
 
+#define C3_MAX_CURVE 16
+
+/* One row of the one-time lookup table of kernel slowdowns (Section V-C): a kernel's time on
+ * cus_per_xcc[i] CUs of every XCC relative to its time on all CUs. */
+typedef struct {
+    int32_t n;                          /* entries used, 1..C3_MAX_CURVE */
+    int32_t reserved;
+    int32_t cus_per_xcc[C3_MAX_CURVE];  /* distinct, each in [1, CUs per XCC] */
+    double slowdown[C3_MAX_CURVE];      /* T(cus_per_xcc[i]) / T(all CUs), > 0 */
+} c3_slowdown_curve;
+
 /* Derived metrics of one concurrent run (abstract; Section IV-B3, Fig. 7). */
 typedef struct {
     double ideal_speedup;   /* (T_gemm + T_copy) / max(T_gemm, T_copy) */
@@ -316,6 +327,29 @@ c3_status c3_run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const 
  * (Abstract; Section III; Section IV-B3.) */
 c3_status c3_derive_metrics(double t_gemm, double t_copy, double t_conc, double bytes_total,
                             double bandwidth, c3_metrics* out);
+
+/* ---------------------------------------------------------------------------------------------
+ * CU-partitioning heuristic (host arithmetic only; no device work)
+ * ------------------------------------------------------------------------------------------- */
+
+/* Roofline time estimate: *t_out = max(flops / (efficiency * peak_flops),
+ * bytes / (efficiency * peak_bw)). The paper's heuristic uses efficiency 0.70 (Section V-C).
+ * Needs flops, bytes >= 0, peaks > 0, 0 < efficiency <= 1. */
+c3_status c3_roofline_time(double flops, double bytes, double peak_flops, double peak_bw,
+                           double efficiency, double* t_out);
+
+/* Choose how many CUs per XCC to give a CU-based collective running beside a GEMM (resource
+ * partitioning, Section V-B; heuristic, Section V-C). For each candidate options[i] = c
+ * (0 < c < cus_per_xcc) the predicted concurrent time is
+ *     max(t_gemm * S_G(cus_per_xcc - c), t_comm * S_C(c)),
+ * S looked up (not interpolated) in the two curves; a value the curve lacks is C3_E_INVALID.
+ * *chosen_out = the option with the smallest prediction (ties: the smaller c);
+ * predicted_out (host array of n_options, may be NULL) receives every prediction in order.
+ * t_gemm, t_comm >= 0 (measured isolated times or c3_roofline_time estimates). */
+c3_status c3_predict_partition(const c3_slowdown_curve* gemm, const c3_slowdown_curve* comm,
+                               double t_gemm, double t_comm, int cus_per_xcc,
+                               const int32_t* options, int n_options, int32_t* chosen_out,
+                               double* predicted_out);
 
 #ifdef __cplusplus
 }

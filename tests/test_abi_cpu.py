@@ -60,7 +60,7 @@ def test_struct_layouts_match_c_compiler(c3, tmp_path):
     import subprocess
 
     structs = [c3.c3_info, c3.c3_move_opts, c3.c3_gemm_args, c3.c3_copy_args, c3.c3_conc_opts,
-               c3.c3_timing, c3.c3_metrics]
+               c3.c3_timing, c3.c3_metrics, c3.c3_slowdown_curve]
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "c3.h"', "int main(void) {"]
     want = []
     for st in structs:
@@ -111,3 +111,32 @@ def test_metrics_agree_with_oracle(c3):
     assert math.isnan(c3.c3_derive_metrics(1.0, 0.0, 1.0)["uplift_fraction"])
     with pytest.raises(c3.C3Error):
         c3.c3_derive_metrics(0.0, 0.0, 1.0)
+
+
+def test_partition_heuristic_matches_oracle(c3):
+    """libc3's host-side heuristic against the oracle's: same choice and bit-identical
+    predictions on random tables; same rejections."""
+    import random
+
+    from oracle import partition as P
+
+    rng = random.Random(12)
+    opts = (1, 2, 4, 8, 16)
+    for trial in range(300):
+        g = {32 - c: rng.uniform(1.0, 3.0) for c in opts}
+        cm = {c: rng.uniform(0.5, 20.0) for c in opts}
+        if trial % 7 == 0:  # force ties
+            cm = {c: 1.0 for c in opts}
+            g = {32 - c: 1.0 for c in opts}
+        tg, tc = rng.uniform(0, 5), rng.uniform(0, 5)
+        want = P.predict_partition(g, cm, tg, tc, 32, opts)
+        got = c3.c3_predict_partition(g, cm, tg, tc, 32, opts)
+        assert got[0] == want[0] and got[1] == want[1], (trial, got, want)
+    for f, b in ((2.0 * 8192 ** 3, 6.0 * 8192 ** 2), (0.0, 2.0 ** 31), (1e9, 1e9)):
+        assert c3.c3_roofline_time(f, b, 2.5e15, 8e12) == P.roofline_time(f, b, 2.5e15, 8e12)
+    with pytest.raises(c3.C3Error):
+        c3.c3_predict_partition({31: 1.0}, {1: 1.0}, 1.0, 1.0, 32, (2,))
+    with pytest.raises(c3.C3Error):
+        c3.c3_predict_partition({31: 1.0}, {1: 1.0}, 1.0, 1.0, 32, (32,))
+    with pytest.raises(c3.C3Error):
+        c3.c3_roofline_time(1.0, 1.0, 1.0, 1.0, 0.0)
