@@ -21,6 +21,9 @@ Other modes print one JSON line per measured cell:
   --mode cus       isolated GEMM time and CU-copy GB/s under balanced CU masks
   --mode partition CU-partitioning sweep (c3_rp) over 30 GEMM x collective scenarios and the
                    slowdown-lookup-table heuristic scored against it
+  --mode gemm_vs_vendor  the library's GEMM against torch.matmul (hipBLASLt) on the same
+                   operands, alternating single launches and back-to-back batches (a reference
+                   point for kernel quality; torch's result is not used for anything else)
 
 Prints ONE JSON line on stdout in the default mode. Progress goes to stderr.
 """
@@ -70,9 +73,10 @@ def measured_traffic(kernel: str, w):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--mode", default="c3", choices=["c3", "movers", "grid", "cus", "partition"])
+    p.add_argument("--mode", default="c3",
+                   choices=["c3", "movers", "grid", "cus", "partition", "gemm_vs_vendor"])
     p.add_argument("--workload", type=int, default=2, help="workload id (1..6)")
     p.add_argument("--gather-mib", type=int, default=0, help="workload 5: total gather MiB")
     p.add_argument("--keep-per-xcc", type=int, default=0,
@@ -187,6 +191,43 @@ class Setup:
             raise SystemExit(f"{label}: C differs from the isolated GEMM")
 
 
+def gpu_state() -> dict | None:
+    """Current shader / memory clock levels, power and temperatures of the AMD GPUs, read from the
+    driver's sysfs files (no child process), or None when they are not readable."""
+    import glob
+
+    def read(path):
+        try:
+            with open(path) as f:
+                return f.read().strip()
+        except OSError:
+            return None
+
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card[0-9]*/device")):
+        if read(os.path.join(dev, "vendor")) != "0x1002":
+            continue
+        st = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+            txt = read(os.path.join(dev, name))
+            if txt:
+                cur = [ln for ln in txt.splitlines() if ln.rstrip().endswith("*")]
+                st[name] = cur[0].split(":", 1)[-1].strip(" *") if cur else txt.splitlines()[-1]
+        for hw in glob.glob(os.path.join(dev, "hwmon", "hwmon*")):
+            for fname, key, scale in (("power1_average", "power_w", 1e-6), ("power1_input", "power_w", 1e-6),
+                                      ("temp1_input", "temp_edge_c", 1e-3), ("temp2_input", "temp_junction_c", 1e-3),
+                                      ("temp3_input", "temp_mem_c", 1e-3), ("freq1_input", "sclk_mhz", 1e-6)):
+                v = read(os.path.join(hw, fname))
+                if v is not None and key not in st:
+                    try:
+                        st[key] = round(int(v) * scale, 1)
+                    except ValueError:
+                        pass
+        if st:
+            out[os.path.basename(os.path.dirname(dev))] = st
+    return out or None
+
+
 def cpu_baseline_and_parity(args, s, w, oracle_seconds):
     """The oracle as it stands, on a bounded sample of the workload (rows 0..r-1 of C, sized to
     take about `oracle_seconds` on the host cores), timed; then those rows are compared with the
@@ -209,10 +250,19 @@ def cpu_baseline_and_parity(args, s, w, oracle_seconds):
         raise SystemExit(f"GEMM parity failure vs oracle on rows 0..{r - 1}: {rep}")
     log(f"oracle rows 0..{r - 1}: GPU C within tolerance ({rep['n_diff']} of {rep['n']} elements "
         f"differ by rounding, max scaled err {rep['max_scaled_err']:.2e})")
+    cpu_model = "?"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     cpu = {"value": round(2.0 * r * w.N * w.K / dt / 1e12, 6), "unit": "TFLOP/s",
            "cores": nthreads, "kind": "oracle",
            "sample": f"fp32-accumulate triple-loop GEMM oracle, rows 0..{r - 1} of C "
-                     f"({r}x{w.N}x{w.K}, {2.0 * r * w.N * w.K / 1e9:.1f} GFLOP) in {dt:.1f} s"}
+                     f"({r}x{w.N}x{w.K}, {2.0 * r * w.N * w.K / 1e9:.1f} GFLOP) in {dt:.1f} s "
+                     f"on {nthreads} threads of {os.cpu_count()} logical CPUs ({cpu_model})"}
     parity = {"rows": r, "elements": rep["n"], "differ_by_rounding": rep["n_diff"],
               "max_scaled_err": rep["max_scaled_err"], "frob_rel": rep["frob_rel"]}
     return cpu, parity
@@ -248,6 +298,7 @@ def run_c3(args, c3, info):
     rec = {name: {"t_copy": [], "c_gpu": [], "t_conc": [], "gk": [], "rs": []} for name, _ in movers}
     torch = s.torch
     torch.cuda.synchronize()
+    state_before = gpu_state()
     wall0 = time.time()
     for i in range(args.warmup + args.steps):
         if i == args.warmup:
@@ -279,6 +330,7 @@ def run_c3(args, c3, info):
                 r["gk"].append(t["gemm_gpu_ms"] * 1e-3)
     torch.cuda.synchronize()
     wall = time.time() - wall0
+    state_after = gpu_state()
     T_gemm = statistics.median(t_gemm)
     log(f"isolated GEMM: median {T_gemm * 1e3:.3f} ms  ({flops / T_gemm / 1e12:.1f} TFLOP/s host, "
         f"{flops / statistics.median(g_gpu) / 1e12:.1f} TFLOP/s events)")
@@ -295,6 +347,7 @@ def run_c3(args, c3, info):
         results[name] = {
             "t_copy_ms": T_copy * 1e3, "t_conc_ms": T_conc * 1e3,
             "t_conc_ms_min": min(r["t_conc"]) * 1e3, "t_conc_ms_max": max(r["t_conc"]) * 1e3,
+            "t_conc_ms_median": statistics.median(r["t_conc"]) * 1e3,
             "t_conc_ms_std": (statistics.pstdev(r["t_conc"]) * 1e3) if len(r["t_conc"]) > 1 else 0.0,
             "copy_gbps_isolated": comm_bytes / T_copy / 1e9,
             "copy_gbps_isolated_engine_clock": (comm_bytes / c_gpu_med / 1e9
@@ -378,6 +431,7 @@ def run_c3(args, c3, info):
                     "C bit-identical to the isolated C; isolated C vs the CPU oracle on the "
                     "cpu_baseline rows",
         "gemm_parity_vs_oracle": parity,
+        "gpu_state": {"before": state_before, "after": state_after},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
@@ -668,6 +722,64 @@ def run_partition(args, c3, info):
         "scenarios_where_best_split_beats_shared": sum(x > 1.0 for x in gain_rp_over_sp)}), flush=True)
 
 
+def run_gemm_vs_vendor(args, c3, info):
+    """The library's GEMM and torch.matmul (hipBLASLt) on the same bf16 operands: alternating
+    event-timed single launches (median), then two batches of 20 back-to-back launches each.
+    C of the library is checked bit-identical across its launches."""
+    import torch
+
+    from concurrent_gemm_dma_amd import workloads as wl
+
+    s = torch.cuda.current_stream()
+    shapes = [(w.M, w.N, w.K) for w in (wl.WORKLOADS[2], wl.WORKLOADS[4], wl.WORKLOADS[5], wl.WORKLOADS[3])]
+    shapes.insert(3, (8192, 8192, 8192))
+    for (M, N, K) in shapes:
+        g = torch.Generator(device="cuda").manual_seed(M * 31 + N * 7 + K)
+        A = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        B = (torch.randn(K, N, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        C = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ours, vendor, first = [], [], None
+        for i in range(5 + max(10, args.steps)):
+            ev[0].record(s)
+            c3.c3_gemm(A, B, C, M, N, K, s)
+            ev[1].record(s)
+            ev[2].record(s)
+            D = A @ B
+            ev[3].record(s)
+            torch.cuda.synchronize()
+            if first is None:
+                first = C.clone()
+            elif not torch.equal(C, first):
+                raise SystemExit("gemm_vs_vendor: C changed between launches")
+            if i >= 5:
+                ours.append(ev[0].elapsed_time(ev[1]))
+                vendor.append(ev[2].elapsed_time(ev[3]))
+        b2b = {"ours": [], "vendor": []}
+        for name in ("ours", "vendor", "ours", "vendor"):
+            torch.cuda.synchronize()
+            ev[0].record(s)
+            for _ in range(20):
+                if name == "ours":
+                    c3.c3_gemm(A, B, C, M, N, K, s)
+                else:
+                    D = A @ B
+            ev[1].record(s)
+            torch.cuda.synchronize()
+            b2b[name].append(ev[0].elapsed_time(ev[1]) / 20)
+        f = 2.0 * M * N * K / 1e9
+        print(json.dumps({"mode": "gemm_vs_vendor", "shape": f"{M}x{N}x{K}",
+                          "ours_ms": round(statistics.median(ours), 4),
+                          "vendor_ms": round(statistics.median(vendor), 4),
+                          "ours_tflops": round(f / statistics.median(ours), 1),
+                          "vendor_tflops": round(f / statistics.median(vendor), 1),
+                          "ours_b2b_tflops": [round(f / x, 1) for x in b2b["ours"]],
+                          "vendor_b2b_tflops": [round(f / x, 1) for x in b2b["vendor"]],
+                          "ours_over_vendor": round(statistics.median(vendor) / statistics.median(ours), 4)}),
+              flush=True)
+        del A, B, C, D, first
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -684,7 +796,7 @@ def main():
     info = c3.c3_device_info()
     log("device:", info)
     {"c3": run_c3, "movers": run_movers, "grid": run_grid, "cus": run_cus,
-     "partition": run_partition}[args.mode](args, c3, info)
+     "partition": run_partition, "gemm_vs_vendor": run_gemm_vs_vendor}[args.mode](args, c3, info)
     c3.c3_finalize()
 
 
