@@ -69,6 +69,7 @@ struct GemmPlan {
     void* C = nullptr;
     int M = 0, N = 0, K = 0;
     int kind = 0;          // 0 = 256x256 tile kernel, 1 = skinny split-K kernel
+    int mt = 1;            // skinny: 16-row MFMA tiles per workgroup (1, 2 or 4)
     int splits = 1;        // skinny: K splits (1 = write bf16 directly)
     int k_per_split = 0;
     float* workspace = nullptr;  // skinny, splits > 1: fp32 partials [splits][Mpad][N]

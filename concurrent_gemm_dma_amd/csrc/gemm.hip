@@ -11,9 +11,10 @@
 //   of one C row and the epilogue writes 8-byte runs. B stays K x N in LDS and is read with the
 //   LDS transpose load (ds_read_b64_tr_b16), which hands each lane 4 consecutive k of one
 //   column. Compute-bound shapes use this kernel.
-// * skinny: 16 x 256 tile, K split across workgroups (deterministic: fp32 partials per split,
-//   summed in split order by a second kernel), v_mfma_f32_16x16x32_bf16. For M <= 64, where the
-//   GEMM streams B once and is bound by HBM bandwidth.
+// * skinny: all M (<= 64) rows x 256 columns per workgroup, K split across workgroups
+//   (deterministic: fp32 partials per split, summed in split order by a second kernel),
+//   v_mfma_f32_16x16x32_bf16. For M <= 64, where the GEMM streams B once and is bound by HBM
+//   bandwidth.
 //
 // Global loads and C stores use raw buffer instructions whose resource covers only the valid
 // part of the operand: anything past it reads as zero / is dropped, and ragged M, N, K edges are
@@ -665,36 +666,50 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
 // Skinny (small M) split-K kernel
 // ------------------------------------------------------------------------------------------------
 namespace sk {
-constexpr int BM = 16, BN = 256, BK = 64, NT = 256;
-constexpr int A_STAGE = BM * BK * 2;  // 2 KiB
-constexpr int B_STAGE = BK * BN * 2;  // 32 KiB
-constexpr int STAGE = A_STAGE + B_STAGE;
-constexpr int B_LD = BK * BN / 8 / NT;  // 8
+constexpr int BM = 16, BN = 256, BK = 64, NT = 256;  // BM: one MFMA tile row block
+constexpr int B_STAGE = BK * BN * 2;                 // 32 KiB
+constexpr int B_LD = BK * BN / 8 / NT;               // 8
+constexpr int MAX_MT = 4;                            // up to 64 rows per workgroup
 }  // namespace sk
 
-// grid: x = N tiles of 256, y = K splits, z = M tiles of 16. Each workgroup covers k in
-// [y*k_per_split, min(K, (y+1)*k_per_split)). With splits == 1 it writes bf16 C; otherwise fp32
-// partials to ws[y][m][n] (m < Mpad = 16*gridDim.z).
+// grid: x = N tiles of 256, y = K splits, z = M blocks of 16*MT rows. Each workgroup covers k in
+// [y*k_per_split, min(K, (y+1)*k_per_split)) for all 16*MT of its rows, so B is streamed from
+// memory once whatever M is (<= 64). With splits == 1 it writes bf16 C; otherwise fp32 partials
+// to ws[y][m][n] (m < Mpad = 16*MT*gridDim.z).
+template <int MT>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_skinny(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     float* __restrict__ ws, int M, int N, int K, int k_per_split) {
     using namespace sk;
+    constexpr int ROWS = BM * MT;
+    constexpr int A_STAGE = ROWS * BK * 2;  // MT * 2 KiB
+    constexpr int STAGE = A_STAGE + B_STAGE;
+    constexpr int A_CHUNKS = ROWS * BK / 8;  // 16-byte chunks per stage
+    constexpr int A_LD = (A_CHUNKS + NT - 1) / NT;
     __shared__ __attribute__((aligned(128))) char smem[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int n0 = blockIdx.x * BN;
-    const int m0 = blockIdx.z * BM;
+    const int m0 = blockIdx.z * ROWS;
     const int kbeg = blockIdx.y * k_per_split;
     const int kend = min(K, kbeg + k_per_split);
 
-    // A: 128 chunks (16 rows x 8), threads 0..127 load one each.
+    // A: chunk c = tid + NT*i (c < A_CHUNKS): row c/8, k chunk c%8.
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + (size_t)m0 * K, (int64_t)(M - m0) * K * 2);
-    const int a_row = (tid >> 3) & 15, a_kc = tid & 7;
-    const bool a_loader = tid < 128;
-    const uint32_t a_g0 = (uint32_t)a_row * (uint32_t)K * 2u + (uint32_t)a_kc * 16u;
-    const uint32_t a_s0 = (uint32_t)a_row * 128u + (uint32_t)((a_kc ^ swz_a(a_row)) << 4);
+    uint32_t a_g0[A_LD], a_s0[A_LD];
+    int a_kc[A_LD];
+    bool a_loader[A_LD];
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+        const int c = tid + NT * i;
+        const int row = (c >> 3) % ROWS;
+        a_loader[i] = c < A_CHUNKS;
+        a_kc[i] = c & 7;
+        a_g0[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)a_kc[i] * 16u;
+        a_s0[i] = (uint32_t)row * 128u + (uint32_t)((a_kc[i] ^ swz_a(row)) << 4);
+    }
     // B: same 64 x 256 stage layout as the tile kernel.
     const int b_row = tid >> 5, b_nc = tid & 31;
     const bool b_nvalid = (n0 + b_nc * 8) < N;
@@ -702,7 +717,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_skinny(
     const uint32_t b_gstep = 8u * (uint32_t)N * 2u;
     const uint32_t b_s0 = (uint32_t)b_row * 512u + (uint32_t)((b_nc ^ swz_b(b_row)) << 4);
 
-    // Column operand (A^T, 16 x 32 per MFMA): lane reads row lane%16, k chunk kk*4 + lane/16.
+    // Column operand (A^T, 16 x 32 per MFMA): lane reads row 16*mt + lane%16, k chunk
+    // kk*4 + lane/16.
     const int ar = lane & 15;
     uint32_t a_rd[2];
 #pragma unroll
@@ -720,14 +736,19 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_skinny(
                    (uint32_t)((p & 1) * 8);
     }
 
-    f32x4_t acc[4];
+    f32x4_t acc[MT][4];
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[ni] = f32x4_t{};
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[mt][ni] = f32x4_t{};
 
-    u32x4_t ra, rb[B_LD];
+    u32x4_t ra[A_LD], rb[B_LD];
     auto load_stage = [&](int k0) {
-        const bool a_kvalid = a_loader && (k0 + a_kc * 8) < kend;
-        ra = load16(rA, a_kvalid ? a_g0 + (uint32_t)k0 * 2u : kOOB);
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i) {
+            const bool ok = a_loader[i] && (k0 + a_kc[i] * 8) < kend;
+            ra[i] = load16(rA, ok ? a_g0[i] + (uint32_t)k0 * 2u : kOOB);
+        }
         const __amdgpu_buffer_rsrc_t rB =
             make_rsrc(B + (size_t)k0 * N + n0, ((int64_t)(kend - k0) * N - n0) * 2);
 #pragma unroll
@@ -737,7 +758,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_skinny(
     auto store_stage = [&](int s) {
         char* As = smem + s * STAGE;
         char* Bs = As + A_STAGE;
-        if (a_loader) lds_store16(As, a_s0, ra);
+#pragma unroll
+        for (int i = 0; i < A_LD; ++i)
+            if (a_loader[i]) lds_store16(As, a_s0[i], ra[i]);
 #pragma unroll
         for (int i = 0; i < B_LD; ++i) lds_store16(Bs, b_s0 + (uint32_t)i * 4096u, rb[i]);
     };
@@ -746,12 +769,17 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_skinny(
         const char* Bs = As + A_STAGE;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8_t colop = lds_load16(As, a_rd[kk]);
+            bf16x8_t colop[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) colop[mt] = lds_load16(As, a_rd[kk] + mt * 2048u);
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni) {
                 const bf16x8_t rowop = lds_load_tr8(Bs, b_rd[ni] + kk * 16384u,
                                                     b_rd[ni] + kk * 16384u + 2048u);
-                acc[ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rowop, colop, acc[ni], 0, 0, 0);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[mt][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rowop, colop[mt],
+                                                                          acc[mt][ni], 0, 0, 0);
             }
         }
     };
@@ -770,29 +798,37 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_skinny(
         }
     }
 
-    // lane holds D[n][m] for m = lane%16, n = 64*wave + 16*ni + 4*(lane/16) + v
-    const int ml = lane & 15;
-    const bool mvalid = (m0 + ml) < M;
+    // lane holds D[n][m] for m = 16*mt + lane%16, n = 64*wave + 16*ni + 4*(lane/16) + v
     if (gridDim.y == 1) {
         const __amdgpu_buffer_rsrc_t rC =
             make_rsrc(C + (size_t)m0 * N + n0, ((int64_t)(M - m0) * N - n0) * 2);
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            const int nl = wave * 64 + ni * 16 + 4 * (lane >> 4);
-            const bool ok = mvalid && (n0 + nl) < N;
-            const uint32_t off = ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 2u : kOOB;
-            store8(rC, off, pack_bf16x4(acc[ni][0], acc[ni][1], acc[ni][2], acc[ni][3]));
+        for (int mt = 0; mt < MT; ++mt) {
+            const int ml = mt * BM + (lane & 15);
+            const bool mvalid = (m0 + ml) < M;
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const int nl = wave * 64 + ni * 16 + 4 * (lane >> 4);
+                const bool ok = mvalid && (n0 + nl) < N;
+                const uint32_t off = ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 2u : kOOB;
+                store8(rC, off, pack_bf16x4(acc[mt][ni][0], acc[mt][ni][1], acc[mt][ni][2],
+                                            acc[mt][ni][3]));
+            }
         }
     } else {
-        const int mpad = gridDim.z * BM;
+        const int mpad = gridDim.z * ROWS;
         float* wsb = ws + ((size_t)blockIdx.y * mpad + m0) * N + n0;
         const __amdgpu_buffer_rsrc_t rW = make_rsrc(wsb, ((int64_t)(mpad - m0) * N - n0) * 4);
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-            const int nl = wave * 64 + ni * 16 + 4 * (lane >> 4);
-            const bool ok = (n0 + nl) < N;
-            const uint32_t off = ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 4u : kOOB;
-            store16(rW, off, __builtin_bit_cast(u32x4_t, acc[ni]));
+        for (int mt = 0; mt < MT; ++mt) {
+            const int ml = mt * BM + (lane & 15);
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+                const int nl = wave * 64 + ni * 16 + 4 * (lane >> 4);
+                const bool ok = (n0 + nl) < N;
+                const uint32_t off = ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 4u : kOOB;
+                store16(rW, off, __builtin_bit_cast(u32x4_t, acc[mt][ni]));
+            }
         }
     }
 }
@@ -863,10 +899,13 @@ c3_status gemm_plan(const void* A, const void* B, void* C, int64_t M, int64_t N,
     p.K = (int)K;
     if (M <= 64) {
         p.kind = 1;
-        const int tiles = (int)((N + sk::BN - 1) / sk::BN) * (int)((M + sk::BM - 1) / sk::BM);
+        p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);  // 16-row MFMA tiles per workgroup (one M block)
+        const int tiles = (int)((N + sk::BN - 1) / sk::BN);
         const int n_cu = ctx().info.n_cu > 0 ? ctx().info.n_cu : 256;
+        // As many K splits as keep every workgroup resident at once (two per CU): a partial
+        // second wave of workgroups would idle most of the chip while it runs.
         int splits = env_int("C3_SKINNY_SPLITS", 0);
-        if (splits <= 0) splits = (2 * n_cu + tiles - 1) / tiles;
+        if (splits <= 0) splits = std::max(1, (2 * n_cu) / tiles);
         const int max_splits = std::max(1, (int)(K / (4 * sk::BK)));
         splits = std::max(1, std::min(splits, max_splits));
         int kps = (int)((K + splits - 1) / splits);
@@ -875,7 +914,7 @@ c3_status gemm_plan(const void* A, const void* B, void* C, int64_t M, int64_t N,
         p.splits = splits;
         p.k_per_split = kps;
         if (splits > 1) {
-            const size_t mpad = (size_t)((M + sk::BM - 1) / sk::BM) * sk::BM;
+            const size_t mpad = (size_t)sk::BM * p.mt;
             const size_t need = (size_t)splits * mpad * (size_t)N * sizeof(float);
             Workspace& w = workspaces()[stream];
             if (w.bytes < need) {
@@ -916,16 +955,23 @@ c3_status gemm_enqueue(const GemmPlan& p, hipStream_t stream) {
         return C3_OK;
     }
     const int tiles_n = (p.N + sk::BN - 1) / sk::BN;
-    const int tiles_m = (p.M + sk::BM - 1) / sk::BM;
     if (p.splits > 1 && !p.workspace) return fail(C3_E_INVALID, "split-K plan without workspace");
-    hipLaunchKernelGGL(gemm_bf16_skinny, dim3(tiles_n, p.splits, tiles_m), dim3(sk::NT), 0, stream,
-                       A, B, C, p.workspace, p.M, p.N, p.K, p.k_per_split);
+    const dim3 grid(tiles_n, p.splits, 1);  // M <= 64: one block of 16*mt rows
+    if (p.mt == 1)
+        hipLaunchKernelGGL(gemm_bf16_skinny<1>, grid, dim3(sk::NT), 0, stream, A, B, C, p.workspace,
+                           p.M, p.N, p.K, p.k_per_split);
+    else if (p.mt == 2)
+        hipLaunchKernelGGL(gemm_bf16_skinny<2>, grid, dim3(sk::NT), 0, stream, A, B, C, p.workspace,
+                           p.M, p.N, p.K, p.k_per_split);
+    else
+        hipLaunchKernelGGL(gemm_bf16_skinny<4>, grid, dim3(sk::NT), 0, stream, A, B, C, p.workspace,
+                           p.M, p.N, p.K, p.k_per_split);
     C3_HIP_TRY(hipGetLastError());
     if (p.splits > 1) {
         const int64_t quads = (int64_t)p.M * (p.N / 4);
         const int blocks = (int)((quads + 255) / 256);
         hipLaunchKernelGGL(splitk_reduce, dim3(blocks), dim3(256), 0, stream, p.workspace, C, p.M,
-                           p.N, tiles_m * sk::BM, p.splits);
+                           p.N, sk::BM * p.mt, p.splits);
         C3_HIP_TRY(hipGetLastError());
     }
     return C3_OK;
