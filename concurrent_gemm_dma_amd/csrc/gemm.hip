@@ -742,27 +742,34 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_skinny(
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) acc[mt][ni] = f32x4_t{};
 
-    u32x4_t ra[A_LD], rb[B_LD];
-    auto load_stage = [&](int k0) {
+#ifndef C3_SKINNY_PF
+#define C3_SKINNY_PF 1
+#endif
+    // Register staging sets: with two, the loads run two K steps ahead of the MFMAs. One is the
+    // default: two measured no faster (85-160 us either way for the skinny workloads), so bytes
+    // in flight are not what limits this stream.
+    constexpr int PF = C3_SKINNY_PF;
+    u32x4_t ra[PF][A_LD], rb[PF][B_LD];
+    auto load_stage = [&](int k0, int set) {
 #pragma unroll
         for (int i = 0; i < A_LD; ++i) {
             const bool ok = a_loader[i] && (k0 + a_kc[i] * 8) < kend;
-            ra[i] = load16(rA, ok ? a_g0[i] + (uint32_t)k0 * 2u : kOOB);
+            ra[set][i] = load16(rA, ok ? a_g0[i] + (uint32_t)k0 * 2u : kOOB);
         }
         const __amdgpu_buffer_rsrc_t rB =
             make_rsrc(B + (size_t)k0 * N + n0, ((int64_t)(kend - k0) * N - n0) * 2);
 #pragma unroll
         for (int i = 0; i < B_LD; ++i)
-            rb[i] = load16(rB, b_nvalid ? b_g0 + (uint32_t)i * b_gstep : kOOB);
+            rb[set][i] = load16(rB, b_nvalid ? b_g0 + (uint32_t)i * b_gstep : kOOB);
     };
-    auto store_stage = [&](int s) {
+    auto store_stage = [&](int s, int set) {
         char* As = smem + s * STAGE;
         char* Bs = As + A_STAGE;
 #pragma unroll
         for (int i = 0; i < A_LD; ++i)
-            if (a_loader[i]) lds_store16(As, a_s0[i], ra[i]);
+            if (a_loader[i]) lds_store16(As, a_s0[i], ra[set][i]);
 #pragma unroll
-        for (int i = 0; i < B_LD; ++i) lds_store16(Bs, b_s0 + (uint32_t)i * 4096u, rb[i]);
+        for (int i = 0; i < B_LD; ++i) lds_store16(Bs, b_s0 + (uint32_t)i * 4096u, rb[set][i]);
     };
     auto compute_stage = [&](int s) {
         const char* As = smem + s * STAGE;
@@ -785,17 +792,28 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_skinny(
     };
 
     const int nk = (kend - kbeg + BK - 1) / BK;
-    if (nk > 0) {
-        load_stage(kbeg);
-        store_stage(0);
+    // K step kt computes LDS stage kt%2. Register set indices must be compile-time constants
+    // (a runtime index would put the staging registers in scratch memory), so the loop body
+    // is written for an even and an odd step.
+    auto body = [&](int kt, auto odd_c) {
+        constexpr int ODD = decltype(odd_c)::value;
+        // stage kt+PF into the register set that stage kt held (already stored to LDS)
+        if (kt + PF < nk) load_stage(kbeg + (kt + PF) * BK, PF == 2 ? ODD : 0);
+        compute_stage(ODD);
+        if (kt + 1 < nk) store_stage(ODD ^ 1, PF == 2 ? (ODD ^ 1) : 0);
         __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const int cur = kt & 1;
-            if (kt + 1 < nk) load_stage(kbeg + (kt + 1) * BK);
-            compute_stage(cur);
-            if (kt + 1 < nk) store_stage(cur ^ 1);
-            __syncthreads();
+    };
+    if (nk > 0) {
+        load_stage(kbeg, 0);
+        store_stage(0, 0);
+        if (PF == 2 && nk > 1) load_stage(kbeg + BK, PF - 1);
+        __syncthreads();
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            body(kt, std::integral_constant<int, 0>{});
+            body(kt + 1, std::integral_constant<int, 1>{});
         }
+        if (kt < nk) body(kt, std::integral_constant<int, 0>{});
     }
 
     // lane holds D[n][m] for m = 16*mt + lane%16, n = 64*wave + 16*ni + 4*(lane/16) + v
