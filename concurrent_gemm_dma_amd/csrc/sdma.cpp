@@ -8,8 +8,10 @@
 // * Engines: for a copy from a GPU to itself the copy-engine status call may report no engine,
 //   so the candidates are one engine id per SDMA engine the agent counts, and each candidate is
 //   kept only if a probe copy on it completes byte-exact at initialisation. Chunk c goes to
-//   engine list[c mod n] (round robin), so with the default of one chunk per shard or block the
-//   8 shards of an all-gather spread over the engines.
+//   engine list[c mod n] (round robin). By default every shard or block is one transfer, cut
+//   into equal 256-byte-aligned pieces until there are at least as many transfers as engines:
+//   one engine moves only ~100 GB/s, so the 8 shards of an all-gather as 8 transfers would
+//   leave half of 16 engines idle.
 // * force_copy_on_sdma = true on every call: for a same-device copy ROCr would otherwise use a
 //   blit kernel, i.e. compute units, which would defeat the purpose.
 // * One completion signal per chunk (initial value 1, decremented to 0 by the engine, negative
