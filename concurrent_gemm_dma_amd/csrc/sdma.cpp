@@ -9,9 +9,9 @@
 //   so the candidates are one engine id per SDMA engine the agent counts, and each candidate is
 //   kept only if a probe copy on it completes byte-exact at initialisation. Chunk c goes to
 //   engine list[c mod n] (round robin). By default every shard or block is one transfer, cut
-//   into equal 256-byte-aligned pieces until there are at least as many transfers as engines:
-//   one engine moves only ~100 GB/s, so the 8 shards of an all-gather as 8 transfers would
-//   leave half of 16 engines idle.
+//   into equal 256-byte-aligned pieces (of at least 128 KiB) until there are at least as many
+//   transfers as engines: one engine moves only ~100 GB/s, so the 8 shards of an all-gather as
+//   8 transfers would leave half of 16 engines idle.
 // * force_copy_on_sdma = true on every call: for a same-device copy ROCr would otherwise use a
 //   blit kernel, i.e. compute units, which would defeat the purpose.
 // * One completion signal per chunk (initial value 1, decremented to 0 by the engine, negative
@@ -176,6 +176,9 @@ c3_status sdma_issue(const std::vector<Segment>& segs, const c3_move_opts& o, Sd
     // Default split: one transfer per segment (shard or block), each cut into just enough
     // pieces that there are at least as many transfers as engines (one engine moves only
     // ~100 GB/s, so a gather of 8 shards would otherwise leave half of 16 engines idle).
+    // Pieces stay at least 128 KiB: below that the host-side cost of one more transfer
+    // outweighs the engine time it saves (1 MiB gather: 22 us as 8 transfers, 25 us as 16).
+    constexpr uint64_t kMinPiece = 128 * 1024;
     size_t nonempty = 0;
     for (const Segment& s : segs) nonempty += s.bytes != 0;
     const uint64_t pieces =
@@ -185,7 +188,8 @@ c3_status sdma_issue(const std::vector<Segment>& segs, const c3_move_opts& o, Sd
         if (s.bytes == 0) continue;
         uint64_t step = o.chunk_bytes;
         if (!step) {
-            step = (s.bytes + pieces - 1) / pieces;
+            const uint64_t p = std::max<uint64_t>(1, std::min<uint64_t>(pieces, s.bytes / kMinPiece));
+            step = (s.bytes + p - 1) / p;
             step = (step + 255) & ~uint64_t(255);  // 256-byte multiples keep pieces aligned
         }
         for (uint64_t off = 0; off < s.bytes; off += step)
