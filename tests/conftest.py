@@ -29,10 +29,24 @@ def _announce_gpu_case(request):
     yield
 
 
+_GPU_USED = []
+
+
+@pytest.fixture
+def host_only():
+    """For tests that start child processes (gcc, bench.py): skipped once this process has
+    initialised the GPU, since a child forked after that must not exec another program."""
+    t = sys.modules.get("torch")
+    if _GPU_USED or (t is not None and t.cuda.is_initialized()):
+        pytest.skip("this process has initialised the GPU; no child processes are started")
+
+
 @pytest.fixture(scope="session")
 def c3gpu():
     """libc3 bound to cuda:0. GPU tests fail (never skip) when no GPU is visible."""
     import torch
+
+    _GPU_USED.append(True)
 
     if not torch.cuda.is_available():
         pytest.fail("GPU test run without a visible GPU")

@@ -54,7 +54,7 @@ def test_calls_before_init_are_rejected(c3):
     assert c3.call("c3_device_info", info) == c3.C3_E_NOT_INIT
 
 
-def test_struct_layouts_match_c_compiler(c3, tmp_path):
+def test_struct_layouts_match_c_compiler(c3, tmp_path, host_only):
     """Every binding struct's size and field offsets equal what a C compiler makes of c3.h."""
     import ctypes
     import subprocess

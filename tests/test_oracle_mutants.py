@@ -110,7 +110,7 @@ def test_unmutated_passes(orc):
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_mutant_is_caught(orc, tmp_path, monkeypatch, name):
+def test_mutant_is_caught(orc, tmp_path, monkeypatch, name, host_only):
     before, after = MUTANTS[name]
     text = open(SRC).read()
     assert text.count(before) == 1, f"mutation anchor for {name} not unique"
