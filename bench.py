@@ -82,6 +82,8 @@ def parse():
     p.add_argument("--keep-per-xcc", type=int, default=0,
                    help="GEMM CU mask: CUs kept per XCC (0 = all)")
     p.add_argument("--gemm-first", action="store_true", help="issue the GEMM first")
+    p.add_argument("--sdma-engines", type=int, default=0,
+                   help="SDMA mover: use only the first N engines found (0 = all)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--profile", action="store_true",
@@ -283,7 +285,12 @@ def run_c3(args, c3, info):
     gmask = c3.c3_cu_mask_balanced(args.keep_per_xcc) if args.keep_per_xcc else None
     comm_first = not args.gemm_first
     movers = (("sdma", c3.C3_MOVER_SDMA), ("cu", c3.C3_MOVER_CU))
-    copy_args = {name: s.cargs(mv) for name, mv in movers}
+    sdma_opts = None
+    if args.sdma_engines:
+        engines = [1 << b for b in range(32) if info["sdma_engine_mask"] >> b & 1][:args.sdma_engines]
+        sdma_opts = c3.move_opts(engine_mask=sum(engines))
+    copy_args = {name: s.cargs(mv, sdma_opts if mv == c3.C3_MOVER_SDMA else None)
+                 for name, mv in movers}
     conc = {}
     for name, mv in movers:
         cmask = None
@@ -408,7 +415,8 @@ def run_c3(args, c3, info):
                         f"{w.units}{'x' + str(w.units) if w.copy == 'all2all' else ''} x "
                         f"{w.unit_bytes / MiB:g} MiB; value = SDMA mover, "
                         f"{'comm-first' if comm_first else 'GEMM-first'}, "
-                        f"GEMM CUs {'all' if not gmask else str(args.keep_per_xcc) + '/XCC'}",
+                        f"GEMM CUs {'all' if not gmask else str(args.keep_per_xcc) + '/XCC'}"
+                        f"{', SDMA engines ' + str(args.sdma_engines) if args.sdma_engines else ''}",
             "M": M, "N": N, "K": K, "copy_bytes": copy_bytes, "comm_hbm_bytes": comm_bytes,
         },
         "copy_gbps_concurrent": round(head["copy_gbps_concurrent"], 1),
