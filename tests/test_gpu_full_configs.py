@@ -1,7 +1,8 @@
-"""Parity at the five workloads' full sizes, in the launch configuration the benchmark times
-(c3_run_concurrent, both movers): the whole copy destination byte-exact, the GEMM checked on
-sampled outputs (random elements, corners, a full row and a full column) against the oracle,
-and bit-exact at full shape with small-integer operands (where the result is unique)."""
+"""Parity at the workloads' full sizes, in the launch configuration the benchmark times
+(c3_run_concurrent, both movers): the whole copy destination byte-exact (for the all-reduce: the
+whole reduced chunk and the whole gathered output bit-exact), the GEMM checked on sampled outputs
+(random elements, corners, a full row and a full column) against the oracle, and bit-exact at
+full shape with small-integer operands (where the result is unique)."""
 import numpy as np
 import pytest
 
@@ -23,10 +24,19 @@ def run_workload(c3, w, int_exact=False, movers=("sdma", "cu"), n_samples=1024):
     A, B = wl.gen_gemm_operands(w, int_exact=int_exact)
     dA, dB = to_dev(A), to_dev(B)
     dC = empty_bf16((w.M, w.N))
+    reduced = want_red = None
     if w.copy == "gather":
         src_np = wl.gen_shards(w)
         src = [to_dev(s) for s in src_np]
         want = oracle.gather(src_np)
+    elif w.copy == "allreduce":
+        contribs, peers = wl.gen_allreduce(w)
+        src = [to_dev(c) for c in contribs]
+        dpeers = [None if p is None else to_dev(p) for p in peers]
+        want_red, want = oracle.allreduce_local(contribs, peers, wl.ALLREDUCE_RANK)
+        want_red, want = want_red.view(np.uint8), want.view(np.uint8)
+        reduced = empty_bytes(want_red.size)
+        src_np = contribs
     else:
         src_np = wl.gen_a2a_source(w)
         src = to_dev(src_np)
@@ -40,10 +50,15 @@ def run_workload(c3, w, int_exact=False, movers=("sdma", "cu"), n_samples=1024):
     for r, mover in enumerate(movers):
         dC.fill_(-1 - r)
         dst.fill_(0x5A + r)
+        if reduced is not None:
+            reduced.fill_(0x3C + r)
         sync()
         m = c3.C3_MOVER_SDMA if mover == "sdma" else c3.C3_MOVER_CU
         if w.copy == "gather":
             cargs, _keep = c3.gather_args(dst, src, w.unit_bytes, m)
+        elif w.copy == "allreduce":
+            cargs, _keep = c3.allreduce_args(dst, reduced, src, dpeers, wl.ALLREDUCE_RANK,
+                                             w.unit_bytes, m)
         else:
             cargs, _keep = c3.all2all_args(dst, src, w.units, w.unit_bytes, m)
         t = c3.c3_run_concurrent(c3.gemm_args(dA, dB, dC, w.M, w.N, w.K), cargs,
@@ -51,6 +66,9 @@ def run_workload(c3, w, int_exact=False, movers=("sdma", "cu"), n_samples=1024):
         print(f"workload {w.wid} ({w.name}) mover={mover} int_exact={int_exact}: "
               f"t_conc={t['t_conc_ns'] / 1e6:.3f} ms", flush=True)
         assert oracle.first_diff(want, bytes_from_dev(dst)) == -1, f"copy mismatch ({mover})"
+        if reduced is not None:
+            assert oracle.first_diff(want_red, bytes_from_dev(reduced)) == -1, \
+                f"reduce-scatter mismatch ({mover})"
         got = bf16_from_dev(dC)
         sampled = got[rows, cols]
         if int_exact:
@@ -66,7 +84,7 @@ def run_workload(c3, w, int_exact=False, movers=("sdma", "cu"), n_samples=1024):
     return first_c
 
 
-@pytest.mark.parametrize("wid", [1, 2, 3, 4])
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 6])
 def test_full_workload(c3gpu, wid):
     run_workload(c3gpu, wl.WORKLOADS[wid])
 
