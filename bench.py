@@ -84,6 +84,8 @@ def parse():
     p.add_argument("--gemm-first", action="store_true", help="issue the GEMM first")
     p.add_argument("--sdma-engines", type=int, default=0,
                    help="SDMA mover: use only the first N engines found (0 = all)")
+    p.add_argument("--cu-nontemporal", action="store_true",
+                   help="CU mover: streaming (non-temporal) loads and stores")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--profile", action="store_true",
@@ -289,7 +291,8 @@ def run_c3(args, c3, info):
     if args.sdma_engines:
         engines = [1 << b for b in range(32) if info["sdma_engine_mask"] >> b & 1][:args.sdma_engines]
         sdma_opts = c3.move_opts(engine_mask=sum(engines))
-    copy_args = {name: s.cargs(mv, sdma_opts if mv == c3.C3_MOVER_SDMA else None)
+    cu_opts = c3.move_opts(nontemporal=1) if args.cu_nontemporal else None
+    copy_args = {name: s.cargs(mv, sdma_opts if mv == c3.C3_MOVER_SDMA else cu_opts)
                  for name, mv in movers}
     conc = {}
     for name, mv in movers:
@@ -416,7 +419,8 @@ def run_c3(args, c3, info):
                         f"{w.unit_bytes / MiB:g} MiB; value = SDMA mover, "
                         f"{'comm-first' if comm_first else 'GEMM-first'}, "
                         f"GEMM CUs {'all' if not gmask else str(args.keep_per_xcc) + '/XCC'}"
-                        f"{', SDMA engines ' + str(args.sdma_engines) if args.sdma_engines else ''}",
+                        f"{', SDMA engines ' + str(args.sdma_engines) if args.sdma_engines else ''}"
+                        f"{', CU copy non-temporal' if args.cu_nontemporal else ''}",
             "M": M, "N": N, "K": K, "copy_bytes": copy_bytes, "comm_hbm_bytes": comm_bytes,
         },
         "copy_gbps_concurrent": round(head["copy_gbps_concurrent"], 1),
