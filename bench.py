@@ -15,9 +15,15 @@ sample of C's rows (timed), which are then compared with the GPU's rows (untimed
 `--workload 6` runs the same protocol on the all-reduce workload (reduce-scatter on the CUs,
 all-gather by the mover under test).
 
+A third cell, the hybrid mover (every copy segment split between the SDMA engines and the CU
+kernel, the engines' share chosen by c3_hybrid_share from isolated times measured in untimed
+runs before the timed rounds), runs beside the two; `--hybrid-permille` fixes the share, -2
+drops the cell. The headline value stays the SDMA mover's.
+
 Other modes print one JSON line per measured cell:
   --mode movers    isolated copy GB/s vs size, CU mover variants and SDMA engine/chunk counts
-  --mode grid      the GC-equal workload's gather-size sweep: mover x GEMM CU mask x order
+  --mode grid      the GC-equal workload's gather-size sweep: mover (CU, SDMA, hybrid) x GEMM
+                   CU mask x order
   --mode cus       isolated GEMM time and CU-copy GB/s under balanced CU masks
   --mode partition CU-partitioning sweep (c3_rp) over 30 GEMM x collective scenarios and the
                    slowdown-lookup-table heuristic scored against it
@@ -86,6 +92,10 @@ def parse():
                    help="SDMA mover: use only the first N engines found (0 = all)")
     p.add_argument("--cu-nontemporal", action="store_true",
                    help="CU mover: streaming (non-temporal) loads and stores")
+    p.add_argument("--hybrid-permille", type=int, default=-1,
+                   help="hybrid mover: thousandths of the copy on the SDMA engines (-1 = chosen "
+                        "by c3_hybrid_share from isolated times measured before the timed runs; "
+                        "-2 = no hybrid cell)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--profile", action="store_true",
@@ -294,15 +304,38 @@ def run_c3(args, c3, info):
     cu_opts = c3.move_opts(nontemporal=1) if args.cu_nontemporal else None
     copy_args = {name: s.cargs(mv, sdma_opts if mv == c3.C3_MOVER_SDMA else cu_opts)
                  for name, mv in movers}
+    iso_g_opts = c3.conc_opts(gemm_mask=gmask, flush_bytes=FLUSH_BYTES)
+    iso_c_opts = c3.conc_opts(flush_bytes=FLUSH_BYTES)
+    hybrid_pm = None
+    if args.hybrid_permille != -2:
+        hybrid_pm = args.hybrid_permille
+        if hybrid_pm < 0:
+            # the engines' share from isolated times (best of two untimed runs of each)
+            cal = {"gemm": [], "sdma": [], "cu": []}
+            for _ in range(2):
+                s.poison()
+                cal["gemm"].append(c3.c3_run_concurrent(s.gargs, None, iso_g_opts)["t_conc_ns"])
+                s.verify_c("calibration GEMM")
+                for name in ("sdma", "cu"):
+                    s.poison()
+                    cal[name].append(c3.c3_run_concurrent(None, copy_args[name][0],
+                                                          iso_c_opts)["t_conc_ns"])
+                    s.verify_copy(f"calibration {name} copy")
+            hybrid_pm = c3.c3_hybrid_share(min(cal["gemm"]) * 1e-9, min(cal["sdma"]) * 1e-9,
+                                           min(cal["cu"]) * 1e-9)
+        log(f"hybrid mover: {hybrid_pm / 10:.1f}% of every segment on the SDMA engines")
+        movers += (("hybrid", c3.C3_MOVER_HYBRID),)
+        hy = c3.move_opts(sdma_permille=hybrid_pm, nontemporal=int(args.cu_nontemporal))
+        if sdma_opts is not None:
+            hy.engine_mask = sdma_opts.engine_mask
+        copy_args["hybrid"] = s.cargs(c3.C3_MOVER_HYBRID, hy)
     conc = {}
     for name, mv in movers:
         cmask = None
-        if gmask is not None and (mv == c3.C3_MOVER_CU or w.copy == "allreduce"):
+        if gmask is not None and (mv != c3.C3_MOVER_SDMA or w.copy == "allreduce"):
             cmask = c3.c3_cu_mask_balanced(args.keep_per_xcc, complement=True)
         conc[name] = c3.conc_opts(gemm_mask=gmask, comm_mask=cmask, comm_first=comm_first,
                                   flush_bytes=FLUSH_BYTES)
-    iso_g_opts = c3.conc_opts(gemm_mask=gmask, flush_bytes=FLUSH_BYTES)
-    iso_c_opts = c3.conc_opts(flush_bytes=FLUSH_BYTES)
 
     t_gemm, g_gpu = [], []
     rec = {name: {"t_copy": [], "c_gpu": [], "t_conc": [], "gk": [], "rs": []} for name, _ in movers}
@@ -346,7 +379,8 @@ def run_c3(args, c3, info):
         f"{flops / statistics.median(g_gpu) / 1e12:.1f} TFLOP/s events)")
 
     results = {}
-    best_copy = min(statistics.median(rec[name]["t_copy"]) for name, _ in movers)
+    # the faster of the paper's two movers: a cell cannot look good against its own slow serial time
+    best_copy = min(statistics.median(rec[name]["t_copy"]) for name in ("sdma", "cu"))
     for name, _ in movers:
         r = rec[name]
         T_copy = statistics.median(r["t_copy"])
@@ -365,6 +399,7 @@ def run_c3(args, c3, info):
             "gemm_tflops_concurrent": flops / T_conc / 1e12,
             "copy_gbps_concurrent": comm_bytes / T_conc / 1e9,
             "gemm_kernel_ms_concurrent": statistics.mean(r["gk"]) * 1e3,
+            **({"sdma_permille": hybrid_pm} if name == "hybrid" else {}),
             "speedup_vs_best_serial": (T_gemm + best_copy) / T_conc,
             **({"reduce_scatter_ms_isolated": statistics.median(r["rs"]) * 1e3,
                 "reduce_scatter_gbps_isolated": ((w.units + 1) * w.unit_bytes
@@ -510,13 +545,23 @@ def run_grid(args, c3, info):
         s = Setup(c3, w, check=not args.profile)
         copy_bytes = w.copy_bytes
         rounds = []
+        names = ("cu", "sdma") + (("hybrid",) if args.hybrid_permille != -2 else ())
+        pm = args.hybrid_permille
         for i in range(reps + 1):
             rnd = {}
             s.poison()
             rnd["gemm"] = c3.c3_run_concurrent(s.gargs, None, c3.conc_opts(flush_bytes=FLUSH_BYTES))["t_conc_ns"]
             s.verify_c("grid isolated GEMM")
-            for mname, mv in (("cu", c3.C3_MOVER_CU), ("sdma", c3.C3_MOVER_SDMA)):
-                ca, _keep = s.cargs(mv)
+            for mname in names:
+                if mname == "hybrid":
+                    if pm < 0:  # chosen once, from the untimed first round's isolated times
+                        pm = c3.c3_hybrid_share(rnd["gemm"] * 1e-9, rnd[("copy", "sdma")] * 1e-9,
+                                                rnd[("copy", "cu")] * 1e-9)
+                    mv = c3.C3_MOVER_HYBRID
+                    ca, _keep = s.cargs(mv, c3.move_opts(sdma_permille=pm))
+                else:
+                    mv = c3.C3_MOVER_CU if mname == "cu" else c3.C3_MOVER_SDMA
+                    ca, _keep = s.cargs(mv)
                 s.poison()
                 rnd[("copy", mname)] = c3.c3_run_concurrent(None, ca, c3.conc_opts(flush_bytes=FLUSH_BYTES))["t_conc_ns"]
                 s.verify_copy("grid isolated copy")
@@ -534,7 +579,7 @@ def run_grid(args, c3, info):
                 rounds.append(rnd)
         Tg = statistics.median(r["gemm"] for r in rounds) * 1e-9
         best_copy = min(statistics.median(r[("copy", m)] for r in rounds) for m in ("cu", "sdma")) * 1e-9
-        for mname in ("cu", "sdma"):
+        for mname in names:
             Tc = statistics.median(r[("copy", mname)] for r in rounds) * 1e-9
             for keep in keeps:
                 for cf in (False, True):
@@ -543,6 +588,7 @@ def run_grid(args, c3, info):
                                              PEAK_HBM_GBPS * 1e9)
                     print(json.dumps({
                         "mode": "grid", "gather_mib": total // MiB, "mover": mname,
+                        **({"sdma_permille": pm} if mname == "hybrid" else {}),
                         "gemm_cus_per_xcc": keep, "comm_first": cf,
                         "t_gemm_ms": round(Tg * 1e3, 4), "t_copy_ms": round(Tc * 1e3, 4),
                         "t_conc_ms": round(Tconc * 1e3, 4),

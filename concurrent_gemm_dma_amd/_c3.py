@@ -28,6 +28,7 @@ STATUS_NAMES = {0: "C3_OK", 1: "C3_E_INVALID", 2: "C3_E_HIP", 3: "C3_E_HSA", 4: 
 
 C3_MOVER_CU = 0
 C3_MOVER_SDMA = 1
+C3_MOVER_HYBRID = 2
 C3_COPY_GATHER = 0
 C3_COPY_ALL2ALL = 1
 C3_COPY_ALLREDUCE = 2
@@ -45,7 +46,7 @@ EXPORTS = ("c3_init", "c3_finalize", "c3_last_error", "c3_device_info", "c3_stre
            "c3_stream_destroy", "c3_cu_mask_balanced", "c3_probe_placement", "c3_gemm",
            "c3_gather", "c3_all2all_block", "c3_reduce_scatter", "c3_allreduce_local",
            "c3_flush_llc", "c3_run_concurrent", "c3_derive_metrics", "c3_roofline_time",
-           "c3_predict_partition")
+           "c3_predict_partition", "c3_hybrid_share")
 
 
 class C3Error(RuntimeError):
@@ -74,7 +75,7 @@ class c3_move_opts(ctypes.Structure):
     _fields_ = [("chunk_bytes", ctypes.c_uint64), ("engine_mask", ctypes.c_uint32),
                 ("nontemporal", ctypes.c_int32), ("cu_blocks", ctypes.c_int32),
                 ("timeout_ms", ctypes.c_int32), ("fault_mode", ctypes.c_int32),
-                ("fault_chunk", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("fault_chunk", ctypes.c_int32), ("sdma_permille", ctypes.c_int32)]
 
 
 class c3_gemm_args(ctypes.Structure):
@@ -180,6 +181,7 @@ def load(path: Optional[str] = None):
                                        ctypes.POINTER(ctypes.c_int32), ctypes.c_int,
                                        ctypes.POINTER(ctypes.c_int32),
                                        ctypes.POINTER(ctypes.c_double)]
+    L.c3_hybrid_share.argtypes = [ctypes.c_double] * 3 + [ctypes.POINTER(ctypes.c_int32)]
     for name in EXPORTS:
         if name != "c3_last_error":
             getattr(L, name).restype = st
@@ -421,3 +423,10 @@ def c3_predict_partition(gemm_table, comm_table, t_gemm: float, t_comm: float, c
     check(load().c3_predict_partition(ctypes.byref(g), ctypes.byref(c), t_gemm, t_comm,
                                       cus_per_xcc, opts, len(options), ctypes.byref(chosen), preds))
     return chosen.value, list(preds)
+
+
+def c3_hybrid_share(t_gemm: float, t_sdma: float, t_cu: float) -> int:
+    """Thousandths of every copy segment the hybrid mover gives the SDMA engines."""
+    out = ctypes.c_int32()
+    check(load().c3_hybrid_share(t_gemm, t_sdma, t_cu, ctypes.byref(out)))
+    return out.value

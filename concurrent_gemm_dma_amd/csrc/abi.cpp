@@ -121,22 +121,61 @@ c3_status comm_plan(const c3_copy_args& a, CommPlan* plan) {
     return fail(C3_E_INVALID, "copy: unknown kind %d", a.kind);
 }
 
+c3_status split_movers(int mover, const c3_move_opts& o, const std::vector<Segment>& segs,
+                       MoverSplit* out) {
+    *out = MoverSplit{};
+    if (mover == C3_MOVER_CU) {
+        out->cu = segs;
+        out->use_cu = true;
+        return C3_OK;
+    }
+    if (mover == C3_MOVER_SDMA) {
+        out->dma = segs;
+        out->use_dma = true;
+        return C3_OK;
+    }
+    if (mover != C3_MOVER_HYBRID) return fail(C3_E_INVALID, "unknown mover %d", mover);
+    if (o.sdma_permille < 0 || o.sdma_permille > 1000)
+        return fail(C3_E_INVALID, "hybrid mover: sdma_permille must be in [0, 1000], got %d",
+                    o.sdma_permille);
+    for (const Segment& s : segs) {
+        if (s.bytes == 0) continue;
+        // bytes < 2^64 / 1000 for any buffer that fits a device; 256-byte multiples keep the
+        // CU part's alignment that of the segment
+        uint64_t head = s.bytes;
+        if (o.sdma_permille < 1000)
+            head = (s.bytes / 1000 * (uint64_t)o.sdma_permille +
+                    s.bytes % 1000 * (uint64_t)o.sdma_permille / 1000) & ~uint64_t(255);
+        if (head) out->dma.push_back({s.src, s.dst, head});
+        if (head < s.bytes)
+            out->cu.push_back({static_cast<const char*>(s.src) + head, static_cast<char*>(s.dst) + head,
+                               s.bytes - head});
+    }
+    out->use_dma = !out->dma.empty();
+    out->use_cu = !out->cu.empty();
+    return C3_OK;
+}
+
 // Isolated collective on `stream`: the reduce-scatter (if any) and a CU-mover copy are
 // enqueued; with the SDMA mover the stream is drained first, then the transfers are issued and
-// waited for.
+// waited for; the hybrid mover drains the stream, issues the engines' share, enqueues the CUs'
+// share and waits for the engines.
 c3_status copy_isolated(const c3_copy_args& a, hipStream_t stream) {
     CommPlan plan;
     C3_TRY(comm_plan(a, &plan));
-    if (a.mover != C3_MOVER_CU && a.mover != C3_MOVER_SDMA)
-        return fail(C3_E_INVALID, "unknown mover %d", a.mover);
+    MoverSplit ms;
+    C3_TRY(split_movers(a.mover, a.opts, plan.segs, &ms));
     if (plan.has_reduce) C3_TRY(reduce_enqueue(plan.reduce, stream));
     if (plan.segs.empty()) return C3_OK;
-    if (a.mover == C3_MOVER_CU) return copy_cu_enqueue(plan.segs, a.opts, stream);
+    if (!ms.use_dma) return copy_cu_enqueue(ms.cu, a.opts, stream);
     C3_HIP_TRY(hipStreamSynchronize(stream));
     SdmaOp op;
-    C3_TRY(sdma_issue(plan.segs, a.opts, &op));
+    C3_TRY(sdma_issue(ms.dma, a.opts, &op));
+    c3_status st = C3_OK;
+    if (ms.use_cu) st = copy_cu_enqueue(ms.cu, a.opts, stream);
     c3_timing t{};
-    return sdma_finish(&op, &t);
+    const c3_status st_dma = sdma_finish(&op, &t);
+    return st != C3_OK ? st : st_dma;
 }
 
 }  // namespace c3

@@ -114,6 +114,16 @@ struct CommPlan {
 // Validate a c3_copy_args and turn it into a plan (no launch, no allocation on the device).
 c3_status comm_plan(const c3_copy_args& a, CommPlan* plan);
 
+// The copy segments each mover takes. CU: all on the CUs; SDMA: all on the engines; HYBRID: the
+// first sdma_permille thousandths of every segment (rounded down to 256 bytes) on the engines,
+// the rest on the CUs, empty parts dropped. use_dma / use_cu say whether each side has work.
+struct MoverSplit {
+    std::vector<Segment> dma, cu;
+    bool use_dma = false, use_cu = false;
+};
+c3_status split_movers(int mover, const c3_move_opts& o, const std::vector<Segment>& segs,
+                       MoverSplit* out);
+
 // ---- SDMA (sdma.cpp) ----------------------------------------------------------------------------
 c3_status sdma_discover();
 void sdma_release();

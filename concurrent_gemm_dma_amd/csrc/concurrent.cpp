@@ -16,6 +16,8 @@
 //   Attack 1): the reduce-scatter kernel runs on the communication stream whatever the mover;
 //   a CU-mover all-gather follows it on that stream, an SDMA all-gather is issued by the
 //   polling loop as soon as the reduce-scatter's end event has completed.
+// * Hybrid mover: the engines' share of every segment and the CUs' share run at the same time,
+//   the latter on the communication stream; the copy is complete when both are.
 #include <algorithm>
 #include <array>
 #include <chrono>
@@ -179,33 +181,31 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
     }
     CommPlan cp;
     const std::vector<Segment>& segs = cp.segs;
+    MoverSplit split;
     c3_move_opts mo{};
-    bool sdma = false;
     if (c) {
         C3_TRY(comm_plan(*c, &cp));
         mo = c->opts;
-        if (c->mover == C3_MOVER_SDMA) {
-            sdma = true;
-        } else if (c->mover != C3_MOVER_CU) {
-            return fail(C3_E_INVALID, "unknown mover %d", c->mover);
-        }
-        if (!sdma || cp.has_reduce) C3_TRY(stream_for_role(1, o.comm_cu_mask, &cs));
-        if (g) {
-            const size_t a_b = (size_t)g->M * g->K * 2, b_b = (size_t)g->K * g->N * 2,
-                         c_b = (size_t)g->M * g->N * 2;
-            auto clash = [&](const void* src, const void* dst, size_t n) {
-                return ranges_overlap(dst, n, g->A, a_b) || ranges_overlap(dst, n, g->B, b_b) ||
-                       ranges_overlap(dst, n, g->C, c_b) || ranges_overlap(src, n, g->C, c_b);
-            };
-            for (const Segment& s : segs)
-                if (clash(s.src, s.dst, s.bytes))
-                    return fail(C3_E_OVERLAP, "copy buffers overlap the GEMM's operands");
-            if (cp.has_reduce) {
-                const size_t n = cp.reduce.elems * 2;
-                for (int r = 0; r < cp.reduce.world; ++r)
-                    if (clash(cp.reduce.in[r], cp.reduce.out, n))
-                        return fail(C3_E_OVERLAP, "reduce-scatter buffers overlap the GEMM's operands");
-            }
+        C3_TRY(split_movers(c->mover, mo, cp.segs, &split));
+    }
+    // the communication stream carries the reduce-scatter and the CUs' share of the copy
+    const bool need_cs = c && (split.use_cu || cp.has_reduce);
+    if (need_cs) C3_TRY(stream_for_role(1, o.comm_cu_mask, &cs));
+    if (c && g) {
+        const size_t a_b = (size_t)g->M * g->K * 2, b_b = (size_t)g->K * g->N * 2,
+                     c_b = (size_t)g->M * g->N * 2;
+        auto clash = [&](const void* src, const void* dst, size_t n) {
+            return ranges_overlap(dst, n, g->A, a_b) || ranges_overlap(dst, n, g->B, b_b) ||
+                   ranges_overlap(dst, n, g->C, c_b) || ranges_overlap(src, n, g->C, c_b);
+        };
+        for (const Segment& s : segs)
+            if (clash(s.src, s.dst, s.bytes))
+                return fail(C3_E_OVERLAP, "copy buffers overlap the GEMM's operands");
+        if (cp.has_reduce) {
+            const size_t n = cp.reduce.elems * 2;
+            for (int r = 0; r < cp.reduce.world; ++r)
+                if (clash(cp.reduce.in[r], cp.reduce.out, n))
+                    return fail(C3_E_OVERLAP, "reduce-scatter buffers overlap the GEMM's operands");
         }
     }
     C3_TRY(ensure_events());
@@ -222,9 +222,12 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
     // ---- issue ----
     SdmaOp op;
     c3_status gemm_st = C3_OK, copy_st = C3_OK;
-    bool copy_issued = false, gemm_issued = false;
-    // all-reduce with the SDMA mover: the transfers wait for the reduce-scatter (host-observed)
-    bool reduce_issued = false, sdma_pending = false;
+    bool gemm_issued = false;
+    bool stream_issued = false;  // c0 .. c1 recorded on the communication stream
+    bool reduce_issued = false;
+    bool sdma_issued = false;
+    // the engines' share of an all-reduce waits for the reduce-scatter (host-observed)
+    bool sdma_pending = false;
     auto issue_gemm = [&]() {
         if (hipEventRecord(ev.g0, gs) != hipSuccess) {
             gemm_st = fail(C3_E_HIP, "hipEventRecord failed");
@@ -236,35 +239,35 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
         gemm_issued = gemm_st == C3_OK;
     };
     auto issue_copy = [&]() {
-        if (cp.has_reduce) {
-            if (hipEventRecord(ev.c0, cs) != hipSuccess) {
-                copy_st = fail(C3_E_HIP, "hipEventRecord failed");
-                return;
-            }
-            copy_st = reduce_enqueue(cp.reduce, cs);
-            if (copy_st == C3_OK && hipEventRecord(ev.r1, cs) != hipSuccess)
-                copy_st = fail(C3_E_HIP, "hipEventRecord failed");
+        // with nothing to wait for, the engines go first: their host-side issue is the slower
+        if (split.use_dma && !cp.has_reduce) {
+            copy_st = sdma_issue(split.dma, mo, &op);
             if (copy_st != C3_OK) return;
-            reduce_issued = true;
-            if (sdma) {
-                sdma_pending = true;  // issued from the polling loop
-            } else {
-                copy_st = copy_cu_enqueue(segs, mo, cs);
-                if (copy_st == C3_OK && hipEventRecord(ev.c1, cs) != hipSuccess)
-                    copy_st = fail(C3_E_HIP, "hipEventRecord failed");
-            }
-        } else if (sdma) {
-            copy_st = sdma_issue(segs, mo, &op);
-        } else {
+            sdma_issued = true;
+        }
+        if (need_cs) {
             if (hipEventRecord(ev.c0, cs) != hipSuccess) {
                 copy_st = fail(C3_E_HIP, "hipEventRecord failed");
                 return;
             }
-            copy_st = copy_cu_enqueue(segs, mo, cs);
-            if (copy_st == C3_OK && hipEventRecord(ev.c1, cs) != hipSuccess)
+            if (cp.has_reduce) {
+                copy_st = reduce_enqueue(cp.reduce, cs);
+                if (copy_st == C3_OK && hipEventRecord(ev.r1, cs) != hipSuccess)
+                    copy_st = fail(C3_E_HIP, "hipEventRecord failed");
+                if (copy_st != C3_OK) return;
+                reduce_issued = true;
+            }
+            if (split.use_cu) {
+                copy_st = copy_cu_enqueue(split.cu, mo, cs);
+                if (copy_st != C3_OK) return;
+            }
+            if (hipEventRecord(ev.c1, cs) != hipSuccess) {
                 copy_st = fail(C3_E_HIP, "hipEventRecord failed");
+                return;
+            }
+            stream_issued = true;
         }
-        copy_issued = copy_st == C3_OK;
+        if (split.use_dma && cp.has_reduce) sdma_pending = true;  // issued from the polling loop
     };
 
     const int64_t t0 = now_ns();
@@ -273,16 +276,18 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
     if (c && !o.comm_first) issue_copy();
     const int64_t t_issue = now_ns() - t0;
 
-    // ---- poll for completion ----
-    bool gdone = !gemm_issued, cdone = !copy_issued;
-    bool sdma_issued = sdma && copy_issued && !cp.has_reduce;
+    // ---- poll for completion: the copy is complete when the communication stream's end event
+    // and every engine transfer are ----
+    bool gdone = !gemm_issued;
+    bool cu_done = !stream_issued, dma_done = !(sdma_issued || sdma_pending);
     bool reduce_seen = !reduce_issued;
-    int64_t tg = 0, tc = 0, tr = 0;
-    if (reduce_issued && !copy_issued) {
-        // the reduce-scatter was launched but the step after it failed to launch
-        (void)hipEventSynchronize(ev.r1);
-        reduce_seen = true;
+    if (copy_st != C3_OK) {
+        // a launch failed part way: nothing more is issued; what was is drained below
+        cu_done = dma_done = reduce_seen = true;
+        sdma_pending = false;
     }
+    bool cdone = cu_done && dma_done;
+    int64_t tg = 0, tc = 0, tr = 0;
     while (!(gdone && cdone)) {
         if (!gdone) {
             const hipError_t e = hipEventQuery(ev.g1);
@@ -302,9 +307,9 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
                 if (sdma_pending) {
                     // all-gather on the engines: issued once the reduced chunk exists
                     sdma_pending = false;
-                    copy_st = sdma_issue(segs, mo, &op);
+                    copy_st = sdma_issue(split.dma, mo, &op);
                     if (copy_st == C3_OK) sdma_issued = true;
-                    else cdone = true;
+                    else dma_done = true;
                 }
             } else if (e != hipErrorNotReady) {
                 copy_st = fail(C3_E_HIP, "reduce-scatter completion query failed: %s",
@@ -312,28 +317,26 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
                 reduce_seen = true;
                 if (sdma_pending) {
                     sdma_pending = false;
-                    cdone = true;
+                    dma_done = true;
                 }
             }
         }
-        if (!cdone && !sdma_pending) {
-            if (sdma) {
-                if (sdma_done(op)) {
-                    cdone = true;
-                    tc = now_ns() - t0;
-                } else if (now_ns() > op.deadline_ns) {
-                    cdone = true;  // sdma_finish reports the timeout
-                }
-            } else {
-                const hipError_t e = hipEventQuery(ev.c1);
-                if (e == hipSuccess) {
-                    cdone = true;
-                    tc = now_ns() - t0;
-                } else if (e != hipErrorNotReady) {
-                    copy_st = fail(C3_E_HIP, "copy completion query failed: %s", hipGetErrorString(e));
-                    cdone = true;
-                }
+        if (!cu_done) {
+            const hipError_t e = hipEventQuery(ev.c1);
+            if (e == hipSuccess) {
+                cu_done = true;
+            } else if (e != hipErrorNotReady) {
+                copy_st = fail(C3_E_HIP, "copy completion query failed: %s", hipGetErrorString(e));
+                cu_done = true;
             }
+        }
+        if (!dma_done && !sdma_pending) {
+            if (sdma_done(op)) dma_done = true;
+            else if (now_ns() > op.deadline_ns) dma_done = true;  // sdma_finish reports the timeout
+        }
+        if (!cdone && cu_done && dma_done) {
+            cdone = true;
+            tc = now_ns() - t0;
         }
     }
     const int64_t t1 = now_ns();
@@ -345,9 +348,8 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
     }
     // Make sure nothing is still running before returning (errors included).
     if (gemm_issued) (void)hipEventSynchronize(ev.g1);
-    if (copy_issued && !sdma) (void)hipEventSynchronize(ev.c1);
+    if (cs) (void)hipStreamSynchronize(cs);
     if (reduce_issued) {
-        (void)hipEventSynchronize(ev.r1);
         if (!tr) tr = now_ns() - t0;  // first observed here (the copy finished before a poll saw it)
         float ms = 0.f;
         if (hipEventElapsedTime(&ms, ev.c0, ev.r1) == hipSuccess) t.reduce_gpu_ms = ms;
@@ -364,14 +366,20 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
         float ms = 0.f;
         if (hipEventElapsedTime(&ms, ev.g0, ev.g1) == hipSuccess) t.gemm_gpu_ms = ms;
     }
-    if (copy_issued && !sdma) {
+    if (stream_issued) {
+        // the stream's span covers the reduce-scatter and the CUs' share; the engines' span
+        // (from their own timestamps) covers only their transfers, so an all-reduce adds the
+        // reduce-scatter's kernel time to it
         float ms = 0.f;
-        if (hipEventElapsedTime(&ms, ev.c0, ev.c1) == hipSuccess) t.copy_gpu_ms = ms;
-        t.n_chunks = (int32_t)segs.size();
-    }
-    if (sdma_issued && cp.has_reduce) {
-        // the engines' span covers the all-gather only; add the reduce-scatter's kernel time
-        t.copy_gpu_ms += t.reduce_gpu_ms;
+        const double stream_ms = hipEventElapsedTime(&ms, ev.c0, ev.c1) == hipSuccess ? ms : 0.0;
+        if (sdma_issued) {
+            const double dma_ms = t.copy_gpu_ms + (cp.has_reduce ? t.reduce_gpu_ms : 0.0);
+            t.copy_gpu_ms = std::max(stream_ms, dma_ms);
+            if (split.use_cu) t.n_chunks += (int32_t)split.cu.size();
+        } else {
+            t.copy_gpu_ms = stream_ms;
+            t.n_chunks = (int32_t)split.cu.size();
+        }
     }
     if (t_out) *t_out = t;
     if (gemm_st != C3_OK) return gemm_st;

@@ -3,7 +3,8 @@
 // the CU split between a GEMM and a CU-based collective ("Optimizing ML Concurrent Computation
 // and Communication with GPU DMA Engines", Section V-B resource partitioning, Section V-C
 // heuristic, as the Pith review reports them). The two kernels run on disjoint CUs, so a split
-// is predicted to take as long as the slower of the two under it. Host arithmetic only.
+// is predicted to take as long as the slower of the two under it. Also the share of a copy
+// the hybrid mover gives the SDMA engines. Host arithmetic only.
 #include <cmath>
 
 #include "c3_internal.h"
@@ -74,6 +75,17 @@ c3_status c3_predict_partition(const c3_slowdown_curve* gemm, const c3_slowdown_
         }
     }
     *chosen_out = best_c;
+    return C3_OK;
+}
+
+c3_status c3_hybrid_share(double t_gemm, double t_sdma, double t_cu, int32_t* permille_out) {
+    if (!permille_out) return c3::fail(C3_E_INVALID, "c3_hybrid_share: permille_out is NULL");
+    if (!(t_gemm >= 0) || !(t_sdma > 0) || !(t_cu > 0) || !std::isfinite(t_gemm) ||
+        !std::isfinite(t_sdma) || !std::isfinite(t_cu))
+        return c3::fail(C3_E_INVALID, "c3_hybrid_share: need finite t_gemm >= 0, t_sdma > 0, t_cu > 0");
+    // engines' part f * t_sdma against the GEMM plus the CUs' part, t_gemm + (1 - f) * t_cu
+    const double f = std::fmin(1.0, (t_gemm + t_cu) / (t_sdma + t_cu));
+    *permille_out = (int32_t)std::lround(1000.0 * f);
     return C3_OK;
 }
 

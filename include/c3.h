@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define C3_ABI_VERSION 2
+#define C3_ABI_VERSION 3
 #define C3_MAX_MASK_WORDS 8 /* CU masks cover up to 256 CUs, bit i = CU i as the driver numbers it */
 #define C3_MAX_SEGMENTS 4096
 #define C3_MAX_WORLD 64 /* ranks of a reduce-scatter / all-reduce local share */
@@ -54,7 +54,12 @@ typedef enum {
     C3_E_NOT_INIT = 8     /* c3_init has not succeeded yet */
 } c3_status;
 
-typedef enum { C3_MOVER_CU = 0, C3_MOVER_SDMA = 1 } c3_mover;
+/* C3_MOVER_HYBRID splits every segment of the copy: its first sdma_permille thousandths (rounded
+ * down to a multiple of 256 bytes) go to the SDMA engines, the rest to the CU copy kernel, and
+ * the two parts run at the same time. Not one of the paper's movers: on MI355X the engines move
+ * a device-local copy several times slower than the CUs do, so when the copy is long beside the
+ * GEMM a pure DMA offload makes the run copy-bound; moving part of it on the CUs shortens it. */
+typedef enum { C3_MOVER_CU = 0, C3_MOVER_SDMA = 1, C3_MOVER_HYBRID = 2 } c3_mover;
 typedef enum { C3_COPY_GATHER = 0, C3_COPY_ALL2ALL = 1, C3_COPY_ALLREDUCE = 2 } c3_copy_kind;
 
 /* Test hooks for the SDMA mover, all forced from the host (no GPU fault is ever provoked):
@@ -105,7 +110,9 @@ typedef struct {
     int32_t timeout_ms;    /* SDMA: wait limit per call (0 = 20000 ms) */
     int32_t fault_mode;    /* c3_fault test hook (0 = off) */
     int32_t fault_chunk;   /* chunk index the fault hook applies to */
-    int32_t reserved;
+    int32_t sdma_permille; /* HYBRID: share of every segment moved by the engines, in thousandths
+                              (0..1000; 0 = all on the CUs, 1000 = all on the engines; see
+                              c3_hybrid_share); ignored by the other movers */
 } c3_move_opts;
 
 /* One GEMM, C[M][N] = A[M][K] . B[K][N], bf16 row-major, fp32 accumulation, bf16 result. */
@@ -162,10 +169,10 @@ typedef struct {
     double gemm_gpu_ms;      /* HIP events around the GEMM launch(es) */
     double copy_gpu_ms;      /* CU mover: HIP events; SDMA: last end - first start of the
                                 engines' own copy timestamps (all-reduce: plus the
-                                reduce-scatter's kernel time) */
+                                reduce-scatter's kernel time); HYBRID: the larger of the two */
     int64_t sdma_first_start_ns; /* SDMA timestamps relative to the earliest chunk start */
     int64_t sdma_last_end_ns;
-    int32_t n_chunks;        /* transfers issued (SDMA) or segments copied (CU) */
+    int32_t n_chunks;        /* transfers issued (SDMA) or segments copied (CU); HYBRID: both */
     uint32_t engines_used;   /* SDMA engines that received a chunk */
     int32_t applied_priority;/* always 0 (default priority) */
     int32_t comm_issued_first;
@@ -258,7 +265,10 @@ c3_status c3_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, i
  * n_shards*shard_bytes bytes. Any alignment and size (shard_bytes = 0 is a no-op).
  * CU mover: stream-ordered and asynchronous. SDMA mover: synchronizes `stream` first (the copy
  * has no stream), issues one transfer per shard (or per chunk_bytes piece) round-robin over the
- * engines, and returns when every transfer completed. Sources must not overlap dst.
+ * engines, and returns when every transfer completed. HYBRID mover: synchronizes `stream`,
+ * issues the engines' share, enqueues the CU kernel for the rest on `stream` and returns when
+ * the engines' transfers completed (the CU part is stream-ordered). opt->sdma_permille outside
+ * 0..1000 is C3_E_INVALID. Sources must not overlap dst.
  * (Section VI-B; Pith review skeptic critique "load-bearing attack".) */
 c3_status c3_gather(void* dst, const void* const* shards, int n_shards, size_t shard_bytes,
                     c3_mover mover, const c3_move_opts* opt, void* stream);
@@ -290,7 +300,7 @@ c3_status c3_reduce_scatter(void* out, const void* const* contribs, int world, s
  * reduced. The all-gather starts only after the reduce-scatter completed and is moved by
  * `ag_mover`: CU - both halves stream-ordered and asynchronous on `stream`; SDMA - the
  * reduce-scatter runs on `stream`, the call waits for it, issues the transfers and returns when
- * they completed. dst and reduced must not overlap each other or any contribution or peer.
+ * they completed; HYBRID - as SDMA for the engines' share, the CU share enqueued on `stream`. dst and reduced must not overlap each other or any contribution or peer.
  * (Same passages as c3_reduce_scatter; the all-gather is c3_gather's.) */
 c3_status c3_allreduce_local(void* dst, void* reduced, const void* const* contribs,
                              const void* const* peers, int world, int rank, size_t chunk_bytes,
@@ -316,6 +326,9 @@ c3_status c3_flush_llc(size_t bytes, void* stream);
  * An all-reduce (c->kind = C3_COPY_ALLREDUCE) runs its reduce-scatter on the o->comm_cu_mask
  * stream whatever the mover; with the SDMA mover the host issues the all-gather transfers as
  * soon as it observes the reduce-scatter complete (t_reduce_done_ns).
+ * HYBRID mover: the engines' share is issued first (for an all-reduce, once the reduce-scatter
+ * is observed complete), the CU share runs on the o->comm_cu_mask stream, and the copy is
+ * complete when both are.
  * Library streams are created once per distinct mask and reused. Errors of either operation are
  * reported after both have finished. */
 c3_status c3_run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_conc_opts* o,
@@ -350,6 +363,18 @@ c3_status c3_predict_partition(const c3_slowdown_curve* gemm, const c3_slowdown_
                                double t_gemm, double t_comm, int cus_per_xcc,
                                const int32_t* options, int n_options, int32_t* chosen_out,
                                double* predicted_out);
+
+/* Share of a copy for the SDMA engines under C3_MOVER_HYBRID (host arithmetic only), from the
+ * isolated times of the GEMM (t_gemm; 0 = no GEMM), of the whole copy on the engines (t_sdma)
+ * and of the whole copy on the CUs (t_cu). Model: the engines' share runs beside the GEMM at its
+ * isolated rate, while a CU copy beside a GEMM on the same CUs adds about its own isolated time
+ * to the GEMM's (what MI355X measures for compute-bound GEMMs). The run then takes
+ *     max(f * t_sdma, t_gemm + (1 - f) * t_cu),
+ * smallest at f = (t_gemm + t_cu) / (t_sdma + t_cu), clamped to [0, 1].
+ * *permille_out = f in thousandths, rounded to nearest. Needs t_gemm >= 0, t_sdma > 0, t_cu > 0
+ * (finite), else C3_E_INVALID. Not from the paper: its DMA engines keep pace with CU
+ * collectives at large sizes, MI355X's do not. */
+c3_status c3_hybrid_share(double t_gemm, double t_sdma, double t_cu, int32_t* permille_out);
 
 #ifdef __cplusplus
 }

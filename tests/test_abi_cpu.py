@@ -140,3 +140,34 @@ def test_partition_heuristic_matches_oracle(c3):
         c3.c3_predict_partition({31: 1.0}, {1: 1.0}, 1.0, 1.0, 32, (32,))
     with pytest.raises(c3.C3Error):
         c3.c3_roofline_time(1.0, 1.0, 1.0, 1.0, 0.0)
+
+
+def test_hybrid_share_closed_forms(c3):
+    """The hybrid mover's engine share balances f * t_sdma against t_gemm + (1 - f) * t_cu:
+    closed-form cases, the clamp, and brute force over every permille on random times."""
+    import random
+
+    assert c3.c3_hybrid_share(0.0, 2.0, 2.0) == 500        # no GEMM, equal movers: half each
+    assert c3.c3_hybrid_share(0.0, 3.0, 1.0) == 250        # engines 3x slower: a quarter
+    assert c3.c3_hybrid_share(1.0, 3.0, 1.0) == 500        # (1 + 1) / (3 + 1)
+    assert c3.c3_hybrid_share(10.0, 1.0, 0.25) == 1000     # GEMM outlasts the whole DMA copy
+    assert c3.c3_hybrid_share(1.0, 1.0, 0.25) == 1000      # GEMM as long as the DMA copy: f = 1
+    assert c3.c3_hybrid_share(0.75, 1.0, 0.25) == 800      # (0.75 + 0.25) / (1 + 0.25)
+
+    def model(pm, tg, ts, tc):
+        f = pm / 1000.0
+        return max(f * ts, tg + (1.0 - f) * tc)
+
+    rng = random.Random(5)
+    for _ in range(500):
+        tg, ts, tc = rng.uniform(0, 3), rng.uniform(0.01, 3), rng.uniform(0.01, 3)
+        got = c3.c3_hybrid_share(tg, ts, tc)
+        assert 0 <= got <= 1000
+        best = min(model(pm, tg, ts, tc) for pm in range(1001))
+        # rounding f to thousandths costs at most 0.5/1000 of the slower mover's time
+        assert model(got, tg, ts, tc) <= best + 0.5e-3 * max(ts, tc) + 1e-12, (tg, ts, tc, got)
+    for bad in ((-1.0, 1.0, 1.0), (1.0, 0.0, 1.0), (1.0, 1.0, 0.0), (float("nan"), 1.0, 1.0),
+                (1.0, float("inf"), 1.0)):
+        with pytest.raises(c3.C3Error):
+            c3.c3_hybrid_share(*bad)
+
