@@ -21,12 +21,15 @@ runs before the timed rounds), runs beside the two; `--hybrid-permille` fixes th
 drops the cell. The headline value stays the SDMA mover's.
 
 Other modes print one JSON line per measured cell:
-  --mode movers    isolated copy GB/s vs size, CU mover variants and SDMA engine/chunk counts
+  --mode movers    isolated copy GB/s vs size, CU mover variants, SDMA engine/chunk counts and
+                   hybrid shares
   --mode grid      the GC-equal workload's gather-size sweep: mover (CU, SDMA, hybrid) x GEMM
                    CU mask x order
   --mode cus       isolated GEMM time and CU-copy GB/s under balanced CU masks
   --mode partition CU-partitioning sweep (c3_rp) over 30 GEMM x collective scenarios and the
                    slowdown-lookup-table heuristic scored against it
+  --mode hybrid    the hybrid mover's concurrent time against its engine share on 8 workloads,
+                   and the share c3_hybrid_share picks scored against the best of the sweep
   --mode gemm_vs_vendor  the library's GEMM against torch.matmul (hipBLASLt) on the same
                    operands, alternating single launches and back-to-back batches (a reference
                    point for kernel quality; torch's result is not used for anything else)
@@ -82,7 +85,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--mode", default="c3",
-                   choices=["c3", "movers", "grid", "cus", "partition", "gemm_vs_vendor"])
+                   choices=["c3", "movers", "grid", "cus", "partition", "gemm_vs_vendor",
+                            "hybrid"])
     p.add_argument("--workload", type=int, default=2, help="workload id (1..6)")
     p.add_argument("--gather-mib", type=int, default=0, help="workload 5: total gather MiB")
     p.add_argument("--keep-per-xcc", type=int, default=0,
@@ -521,6 +525,10 @@ def run_movers(args, c3, info):
         for chunks in (16, 32, 64):
             cells.append(("sdma", f"{len(engines)} engines, {chunks} chunks", c3.C3_MOVER_SDMA,
                           c3.move_opts(chunk_bytes=max(4096, S // chunks))))
+        # both at once: the engines' bandwidth on top of the CUs' (balanced near 200 per mille)
+        for pm in (100, 150, 200, 250, 300):
+            cells.append(("hybrid", f"{pm} per mille on the engines", c3.C3_MOVER_HYBRID,
+                          c3.move_opts(sdma_permille=pm)))
         for mover, label, mv, opts in cells:
             T, G, eng, nch = time_copy(c3, s, mv, opts, reps)
             print(json.dumps({"mode": "movers", "total_mib": total_mib, "mover": mover,
@@ -838,6 +846,75 @@ def run_gemm_vs_vendor(args, c3, info):
         del A, B, C, D, first
 
 
+def run_hybrid(args, c3, info):
+    """Hybrid mover: concurrent time against the engines' share of the copy (0..1000 per mille in
+    steps of 100), the share c3_hybrid_share picks from the isolated times, and its loss against
+    the best share of the sweep."""
+    from concurrent_gemm_dma_amd import workloads as wl
+
+    cases = [(5, g) for g in (128, 256, 512, 768, 1024)] + [(3, 0), (6, 0), (4, 0)]
+    shares = list(range(0, 1001, 100))
+    reps = max(3, args.steps)
+    flush = c3.conc_opts(flush_bytes=FLUSH_BYTES)
+    conc_opts = c3.conc_opts(comm_first=True, flush_bytes=FLUSH_BYTES)
+    for wid, gmib in cases:
+        w = wl.WORKLOADS[wid]
+        if gmib:
+            w = w.with_gather_total(gmib * MiB)
+        s = Setup(c3, w, check=not args.profile)
+        iso = {"gemm": [], "sdma": [], "cu": []}
+        pure = {"sdma": s.cargs(c3.C3_MOVER_SDMA), "cu": s.cargs(c3.C3_MOVER_CU)}
+        hyb = {pm: s.cargs(c3.C3_MOVER_HYBRID, c3.move_opts(sdma_permille=pm)) for pm in shares}
+        conc = {pm: [] for pm in shares}
+
+        def conc_run(pm, ca, out, timed):
+            s.poison()
+            t = c3.c3_run_concurrent(s.gargs, ca, conc_opts)
+            s.verify_copy(f"hybrid {pm}")
+            s.verify_c(f"hybrid {pm}")
+            if timed:
+                out.append(t["t_conc_ns"] * 1e-9)
+
+        for i in range(reps + 1):
+            timed = i > 0
+            s.poison()
+            t = c3.c3_run_concurrent(s.gargs, None, flush)
+            s.verify_c("hybrid sweep isolated GEMM")
+            if timed:
+                iso["gemm"].append(t["t_conc_ns"] * 1e-9)
+            for name, (ca, _keep) in pure.items():
+                s.poison()
+                t = c3.c3_run_concurrent(None, ca, flush)
+                s.verify_copy(f"hybrid sweep isolated {name}")
+                if timed:
+                    iso[name].append(t["t_conc_ns"] * 1e-9)
+            for pm in shares:
+                conc_run(pm, hyb[pm][0], conc[pm], timed)
+        med = {k: statistics.median(v) for k, v in iso.items()}
+        chosen = c3.c3_hybrid_share(med["gemm"], med["sdma"], med["cu"])
+        if chosen not in conc:
+            ca = s.cargs(c3.C3_MOVER_HYBRID, c3.move_opts(sdma_permille=chosen))
+            conc[chosen] = []
+            for i in range(reps + 1):
+                conc_run(chosen, ca[0], conc[chosen], i > 0)
+        mean = {pm: statistics.mean(v) for pm, v in conc.items()}
+        best = min(mean, key=lambda pm: mean[pm])
+        serial = med["gemm"] + min(med["sdma"], med["cu"])
+        print(json.dumps({
+            "mode": "hybrid", "workload": w.name, "copy": w.copy,
+            "copy_mib": round(w.copy_bytes / MiB, 1),
+            "t_gemm_ms": round(med["gemm"] * 1e3, 4), "t_sdma_ms": round(med["sdma"] * 1e3, 4),
+            "t_cu_ms": round(med["cu"] * 1e3, 4),
+            "t_conc_ms": {str(pm): round(mean[pm] * 1e3, 4) for pm in sorted(mean)},
+            "chosen_permille": chosen, "t_chosen_ms": round(mean[chosen] * 1e3, 4),
+            "best_permille": best, "t_best_ms": round(mean[best] * 1e3, 4),
+            "loss_vs_best": round(mean[chosen] / mean[best] - 1, 4),
+            "chosen_vs_sdma_only": round(mean[1000] / mean[chosen], 4),
+            "chosen_vs_cu_only": round(mean[0] / mean[chosen], 4),
+            "chosen_vs_best_serial": round(serial / mean[chosen], 4)}), flush=True)
+        del s
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -853,7 +930,7 @@ def main():
     c3.c3_init(0)
     info = c3.c3_device_info()
     log("device:", info)
-    {"c3": run_c3, "movers": run_movers, "grid": run_grid, "cus": run_cus,
+    {"c3": run_c3, "movers": run_movers, "grid": run_grid, "cus": run_cus, "hybrid": run_hybrid,
      "partition": run_partition, "gemm_vs_vendor": run_gemm_vs_vendor}[args.mode](args, c3, info)
     c3.c3_finalize()
 

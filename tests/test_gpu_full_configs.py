@@ -1,8 +1,8 @@
 """Parity at the workloads' full sizes, in the launch configuration the benchmark times
-(c3_run_concurrent, both movers): the whole copy destination byte-exact (for the all-reduce: the
-whole reduced chunk and the whole gathered output bit-exact), the GEMM checked on sampled outputs
-(random elements, corners, a full row and a full column) against the oracle, and bit-exact at
-full shape with small-integer operands (where the result is unique)."""
+(c3_run_concurrent; SDMA, CU and hybrid movers): the whole copy destination byte-exact (for the
+all-reduce: the whole reduced chunk and the whole gathered output bit-exact), the GEMM checked on
+sampled outputs (random elements, corners, a full row and a full column) against the oracle,
+and bit-exact at full shape with small-integer operands (where the result is unique)."""
 import numpy as np
 import pytest
 
@@ -53,14 +53,18 @@ def run_workload(c3, w, int_exact=False, movers=("sdma", "cu"), n_samples=1024):
         if reduced is not None:
             reduced.fill_(0x3C + r)
         sync()
-        m = c3.C3_MOVER_SDMA if mover == "sdma" else c3.C3_MOVER_CU
+        opts = None
+        if mover.startswith("hybrid:"):  # "hybrid:<engines' share in thousandths>"
+            m, opts = c3.C3_MOVER_HYBRID, c3.move_opts(sdma_permille=int(mover.split(":")[1]))
+        else:
+            m = c3.C3_MOVER_SDMA if mover == "sdma" else c3.C3_MOVER_CU
         if w.copy == "gather":
-            cargs, _keep = c3.gather_args(dst, src, w.unit_bytes, m)
+            cargs, _keep = c3.gather_args(dst, src, w.unit_bytes, m, opts)
         elif w.copy == "allreduce":
             cargs, _keep = c3.allreduce_args(dst, reduced, src, dpeers, wl.ALLREDUCE_RANK,
-                                             w.unit_bytes, m)
+                                             w.unit_bytes, m, opts)
         else:
-            cargs, _keep = c3.all2all_args(dst, src, w.units, w.unit_bytes, m)
+            cargs, _keep = c3.all2all_args(dst, src, w.units, w.unit_bytes, m, opts)
         t = c3.c3_run_concurrent(c3.gemm_args(dA, dB, dC, w.M, w.N, w.K), cargs,
                                  c3.conc_opts(comm_first=True))
         print(f"workload {w.wid} ({w.name}) mover={mover} int_exact={int_exact}: "
@@ -86,12 +90,13 @@ def run_workload(c3, w, int_exact=False, movers=("sdma", "cu"), n_samples=1024):
 
 @pytest.mark.parametrize("wid", [1, 2, 3, 4, 6])
 def test_full_workload(c3gpu, wid):
-    run_workload(c3gpu, wl.WORKLOADS[wid])
+    run_workload(c3gpu, wl.WORKLOADS[wid], movers=("sdma", "cu", "hybrid:500"))
 
 
 @pytest.mark.parametrize("total_mib", [32, 1024])
 def test_full_gc_equal_sweep_ends(c3gpu, total_mib):
-    run_workload(c3gpu, wl.WORKLOADS[5].with_gather_total(total_mib * MiB), movers=("sdma",))
+    run_workload(c3gpu, wl.WORKLOADS[5].with_gather_total(total_mib * MiB),
+                 movers=("sdma", "hybrid:679"))
 
 
 @pytest.mark.parametrize("wid", [2, 3])
