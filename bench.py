@@ -520,7 +520,7 @@ def run_movers(args, c3, info):
         for n in (1, 2, 4, 8, 16):
             if n <= len(engines):
                 mask = sum(engines[:n])
-                cells.append(("sdma", f"{n} engines, 8 chunks", c3.C3_MOVER_SDMA,
+                cells.append(("sdma", f"{n} engines, default split", c3.C3_MOVER_SDMA,
                               c3.move_opts(engine_mask=mask)))
         for chunks in (16, 32, 64):
             cells.append(("sdma", f"{len(engines)} engines, {chunks} chunks", c3.C3_MOVER_SDMA,
@@ -848,12 +848,11 @@ def run_gemm_vs_vendor(args, c3, info):
 
 def run_hybrid(args, c3, info):
     """Hybrid mover: concurrent time against the engines' share of the copy (0..1000 per mille in
-    steps of 100), the share c3_hybrid_share picks from the isolated times, and its loss against
-    the best share of the sweep."""
+    steps of 100), the share c3_hybrid_share picks from the untimed first round's isolated times
+    (timed in the same rounds as the sweep), and its loss against the best share of the sweep."""
     from concurrent_gemm_dma_amd import workloads as wl
 
     cases = [(5, g) for g in (128, 256, 512, 768, 1024)] + [(3, 0), (6, 0), (4, 0)]
-    shares = list(range(0, 1001, 100))
     reps = max(3, args.steps)
     flush = c3.conc_opts(flush_bytes=FLUSH_BYTES)
     conc_opts = c3.conc_opts(comm_first=True, flush_bytes=FLUSH_BYTES)
@@ -862,41 +861,37 @@ def run_hybrid(args, c3, info):
         if gmib:
             w = w.with_gather_total(gmib * MiB)
         s = Setup(c3, w, check=not args.profile)
+        shares = list(range(0, 1001, 100))
         iso = {"gemm": [], "sdma": [], "cu": []}
         pure = {"sdma": s.cargs(c3.C3_MOVER_SDMA), "cu": s.cargs(c3.C3_MOVER_CU)}
         hyb = {pm: s.cargs(c3.C3_MOVER_HYBRID, c3.move_opts(sdma_permille=pm)) for pm in shares}
         conc = {pm: [] for pm in shares}
-
-        def conc_run(pm, ca, out, timed):
-            s.poison()
-            t = c3.c3_run_concurrent(s.gargs, ca, conc_opts)
-            s.verify_copy(f"hybrid {pm}")
-            s.verify_c(f"hybrid {pm}")
-            if timed:
-                out.append(t["t_conc_ns"] * 1e-9)
-
+        chosen = None
         for i in range(reps + 1):
             timed = i > 0
             s.poison()
             t = c3.c3_run_concurrent(s.gargs, None, flush)
             s.verify_c("hybrid sweep isolated GEMM")
-            if timed:
-                iso["gemm"].append(t["t_conc_ns"] * 1e-9)
+            iso["gemm"].append(t["t_conc_ns"] * 1e-9)
             for name, (ca, _keep) in pure.items():
                 s.poison()
                 t = c3.c3_run_concurrent(None, ca, flush)
                 s.verify_copy(f"hybrid sweep isolated {name}")
+                iso[name].append(t["t_conc_ns"] * 1e-9)
+            if chosen is None:
+                # the rule's share, from this untimed round's isolated times
+                chosen = c3.c3_hybrid_share(iso["gemm"][0], iso["sdma"][0], iso["cu"][0])
+                if chosen not in hyb:
+                    hyb[chosen] = s.cargs(c3.C3_MOVER_HYBRID, c3.move_opts(sdma_permille=chosen))
+                    conc[chosen] = []
+            for pm in sorted(hyb):
+                s.poison()
+                t = c3.c3_run_concurrent(s.gargs, hyb[pm][0], conc_opts)
+                s.verify_copy(f"hybrid {pm}")
+                s.verify_c(f"hybrid {pm}")
                 if timed:
-                    iso[name].append(t["t_conc_ns"] * 1e-9)
-            for pm in shares:
-                conc_run(pm, hyb[pm][0], conc[pm], timed)
-        med = {k: statistics.median(v) for k, v in iso.items()}
-        chosen = c3.c3_hybrid_share(med["gemm"], med["sdma"], med["cu"])
-        if chosen not in conc:
-            ca = s.cargs(c3.C3_MOVER_HYBRID, c3.move_opts(sdma_permille=chosen))
-            conc[chosen] = []
-            for i in range(reps + 1):
-                conc_run(chosen, ca[0], conc[chosen], i > 0)
+                    conc[pm].append(t["t_conc_ns"] * 1e-9)
+        med = {k: statistics.median(v[1:]) for k, v in iso.items()}
         mean = {pm: statistics.mean(v) for pm, v in conc.items()}
         best = min(mean, key=lambda pm: mean[pm])
         serial = med["gemm"] + min(med["sdma"], med["cu"])
@@ -907,6 +902,7 @@ def run_hybrid(args, c3, info):
             "t_cu_ms": round(med["cu"] * 1e3, 4),
             "t_conc_ms": {str(pm): round(mean[pm] * 1e3, 4) for pm in sorted(mean)},
             "chosen_permille": chosen, "t_chosen_ms": round(mean[chosen] * 1e3, 4),
+            "chosen_from_timed_medians": c3.c3_hybrid_share(med["gemm"], med["sdma"], med["cu"]),
             "best_permille": best, "t_best_ms": round(mean[best] * 1e3, 4),
             "loss_vs_best": round(mean[chosen] / mean[best] - 1, 4),
             "chosen_vs_sdma_only": round(mean[1000] / mean[chosen], 4),

@@ -101,7 +101,8 @@ typedef struct {
     uint64_t chunk_bytes;  /* SDMA: split every segment into chunks of at most this many bytes
                               (0 = one transfer per shard or block, the paper's direct scheme,
                               each cut into equal 256-byte-multiple pieces of at least 128 KiB
-                              until there are at least as many transfers as engines) */
+                              until there are at least as many transfers as engines, and into
+                              pieces of at most 16 MiB) */
     uint32_t engine_mask;  /* SDMA: use only these engines (one-hot HSA_AMD_SDMA_ENGINE_i bits;
                               0 = every engine available for device-local copies). Chunk c goes
                               to the (c mod n)-th engine of the mask. */

@@ -99,6 +99,25 @@ def test_sdma_chunks_and_engines(c3gpu):
             assert oracle.first_diff(want, got) == -1, f"engine bit {b}"
 
 
+@pytest.mark.parametrize("n,sb", [(8, 40 * MiB + 256), (8, MiB), (8, 128 * KiB + 5), (3, 20 * MiB),
+                                  (1, 1000)])
+def test_sdma_default_split(c3gpu, n, sb):
+    """Default split: per segment p = max(1, min(ceil(E / segments), bytes // 128 KiB),
+    ceil(bytes / 16 MiB)) equal 256-byte-multiple pieces, E = engines available."""
+    info = c3gpu.c3_device_info()
+    engines = bin(info["sdma_engine_mask"]).count("1")
+    shards_np = [wl.gen_bytes(sb, 8400 + i) for i in range(n)]
+    shards = [to_dev(s) for s in shards_np]
+    dst = empty_bytes(n * sb)
+    cargs, _keep = c3gpu.gather_args(dst, shards, sb, c3gpu.C3_MOVER_SDMA)
+    t = c3gpu.c3_run_concurrent(None, cargs)
+    assert oracle.first_diff(oracle.gather(shards_np), bytes_from_dev(dst)) == -1
+    p = max(1, min(-(-engines // n), sb // (128 * KiB)), -(-sb // (16 * MiB)))
+    step = -(-sb // p)
+    step = (step + 255) // 256 * 256
+    assert t["n_chunks"] == n * -(-sb // step), (t["n_chunks"], p, step)
+
+
 def test_cu_nontemporal_and_block_count(c3gpu):
     shards = [wl.gen_bytes(MiB, 8400 + i) for i in range(8)]
     want = oracle.gather(shards)
