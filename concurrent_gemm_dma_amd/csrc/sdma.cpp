@@ -11,7 +11,8 @@
 //   engine list[c mod n] (round robin). By default every shard or block is one transfer, cut
 //   into equal 256-byte-aligned pieces (of at least 128 KiB) until there are at least as many
 //   transfers as engines: one engine moves only ~100 GB/s, so the 8 shards of an all-gather as
-//   8 transfers would leave half of 16 engines idle.
+//   8 transfers would leave half of 16 engines idle. Pieces are also kept to at most 16 MiB.
+//   The hybrid mover hands this path the engines' share of every segment.
 // * force_copy_on_sdma = true on every call: for a same-device copy ROCr would otherwise use a
 //   blit kernel, i.e. compute units, which would defeat the purpose.
 // * One completion signal per chunk (initial value 1, decremented to 0 by the engine, negative
