@@ -100,6 +100,8 @@ def parse():
                    help="hybrid mover: thousandths of the copy on the SDMA engines (-1 = chosen "
                         "by c3_hybrid_share from isolated times measured before the timed runs; "
                         "-2 = no hybrid cell)")
+    p.add_argument("--shapes", default="",
+                   help="gemm_vs_vendor: comma-separated MxNxK list instead of the workloads' shapes")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--profile", action="store_true",
@@ -799,6 +801,8 @@ def run_gemm_vs_vendor(args, c3, info):
     s = torch.cuda.current_stream()
     shapes = [(w.M, w.N, w.K) for w in (wl.WORKLOADS[2], wl.WORKLOADS[4], wl.WORKLOADS[5], wl.WORKLOADS[3])]
     shapes.insert(3, (8192, 8192, 8192))
+    if args.shapes:
+        shapes = [tuple(int(x) for x in sh.split("x")) for sh in args.shapes.split(",")]
     for (M, N, K) in shapes:
         g = torch.Generator(device="cuda").manual_seed(M * 31 + N * 7 + K)
         A = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)

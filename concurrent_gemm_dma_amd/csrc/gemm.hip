@@ -26,6 +26,12 @@
 #include <map>
 #include <type_traits>
 
+// 1 = the LDS-direct 256x256 tile kernel (with split-K for small tile counts); 0 = the earlier
+// register-staged tile kernel (no split-K), kept for comparison.
+#ifndef C3_GEMM_KERNEL
+#define C3_GEMM_KERNEL 1
+#endif
+
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -389,9 +395,13 @@ __device__ __forceinline__ void lds_dma16(i32x4_t r, char* lds, uint32_t voff) {
     lds_dma16_at(r, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(C3_LDS char*)lds), voff);
 }
 
+// SPLIT = false: the whole K, bf16 C. SPLIT = true: K split y = blockIdx.y, fp32 partials to
+// ws[y][M][N] for splitk_reduce (a template parameter so that the two epilogues never share the
+// register budget of one kernel).
+template <bool SPLIT>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
-    int M, int N, int K, int tiles_m, int tiles_n) {
+    float* __restrict__ ws, int M, int N, int K, int k_per_split, int tiles_m, int tiles_n) {
     using namespace td;
     __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
 
@@ -403,10 +413,18 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     int tm, tn;
     map_tile<GROUP_M>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
+    // K split y = blockIdx.y covers k in [kbeg, kbeg + Ke); A keeps its row stride K.
+    const int kbeg = SPLIT ? blockIdx.y * k_per_split : 0;
+    const int Ke = SPLIT ? min(K, kbeg + k_per_split) - kbeg : K;
+    if (SPLIT) {
+        A += kbeg;
+        B += (size_t)kbeg * N;
+    }
 
     // ---- global -> LDS addressing. Wave w fills A blocks w*4+j (16 rows each) and B blocks
     // w*4+j (2 k rows each), j = 0..3; lane t lands at byte 16*t of the 1 KiB block.
-    const i32x4_t rA = make_rsrc_words(A + (size_t)m0 * K, (int64_t)(M - m0) * K * 2);
+    const i32x4_t rA =
+        make_rsrc_words(A + (size_t)m0 * K, (int64_t)(M - m0) * K * 2 - (int64_t)kbeg * 2);
     const int a_row0 = 16 * (wave * 4) + (lane >> 2);           // + 16*j
     const int a_kc = (lane & 3) ^ swz_a32(a_row0);               // same for every j
     const uint32_t a_g0 = (uint32_t)a_row0 * (uint32_t)K * 2u + (uint32_t)a_kc * 16u;
@@ -423,13 +441,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     auto issue_stage = [&](int k0, int s) {
         char* As = smem + s * STAGE;
         char* Bs = As + A_STAGE;
-        const bool a_ok = (k0 + a_kc * 8) < K;
+        const bool a_ok = (k0 + a_kc * 8) < Ke;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             lds_dma16(rA, As + (wave * 4 + j) * 1024,
                       a_ok ? a_g0 + (uint32_t)j * a_gstep + (uint32_t)k0 * 2u : kOOB);
         const i32x4_t rB =
-            make_rsrc_words(B + (size_t)k0 * N + n0, ((int64_t)(K - k0) * N - n0) * 2);
+            make_rsrc_words(B + (size_t)k0 * N + n0, ((int64_t)(Ke - k0) * N - n0) * 2);
 #pragma unroll
         for (int j = 0; j < 4; ++j) lds_dma16(rB, Bs + (wave * 4 + j) * 1024, b_ok[j] ? b_g[j] : kOOB);
     };
@@ -475,7 +493,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
                                                                       acc[mi][ni], 0, 0, 0);
     };
 
-    const int nk = (K + BK - 1) / BK;
+    const int nk = (Ke + BK - 1) / BK;
 #ifndef C3_GEMM_INTERLEAVE
 #define C3_GEMM_INTERLEAVE 1
 #endif
@@ -490,7 +508,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         if (s < nk) issue_stage(s * BK, s);
     if (nk > NSTAGE - 1) {
         const int k0 = (NSTAGE - 1) * BK;
-        const bool a_ok = (k0 + a_kc * 8) < K;
+        const bool a_ok = (k0 + a_kc * 8) < Ke;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             lds_dma16(rA, smem + (NSTAGE - 1) * STAGE + (wave * 4 + j) * 1024,
@@ -562,7 +580,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         const int s3 = (kt + NSTAGE - 1) & (NSTAGE - 1);
         const int k3 = (kt + NSTAGE - 1) * BK;
         i32x4_t rB3{};
-        if (BA) rB3 = make_rsrc_words(B + (size_t)k3 * N + n0, ((int64_t)(K - k3) * N - n0) * 2);
+        if (BA) rB3 = make_rsrc_words(B + (size_t)k3 * N + n0, ((int64_t)(Ke - k3) * N - n0) * 2);
         const uint32_t b_dst3 = b_dst0 + (uint32_t)s3 * STAGE;
         // first half: MFMAs of k-slice 0 (set 0) with the reads of k-slice 1 (set 1)
 #pragma unroll
@@ -585,9 +603,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         // (set 0) and the refill of this step's buffer for step kt+4
         const int s1 = (kt + 1) & (NSTAGE - 1);
         const int k0 = (kt + NSTAGE) * BK;
-        const bool a_ok = (k0 + a_kc * 8) < K;
+        const bool a_ok = (k0 + a_kc * 8) < Ke;
         i32x4_t rB{};
-        if (RB) rB = make_rsrc_words(B + (size_t)k0 * N + n0, ((int64_t)(K - k0) * N - n0) * 2);
+        if (RB) rB = make_rsrc_words(B + (size_t)k0 * N + n0, ((int64_t)(Ke - k0) * N - n0) * 2);
         const uint32_t a_dst = a_dst0 + (uint32_t)s * STAGE;
         const uint32_t b_dst = b_dst0 + (uint32_t)s * STAGE;
         const uint32_t a_off = a_g0 + (uint32_t)k0 * 2u;
@@ -642,21 +660,48 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     }
 #endif
 
-    const __amdgpu_buffer_rsrc_t rC =
-        make_rsrc(C + (size_t)m0 * N + n0, ((int64_t)(M - m0) * N - n0) * 2);
+    // ---- epilogue: lane holds C[m][n..n+3], m = mi*32 + lane%32, n = ni*32 + 8g + 4*(lane/32);
+    // one K split writes bf16 C, several write fp32 partials ws[y][m][n] for splitk_reduce
+    if (!SPLIT) {
+        const __amdgpu_buffer_rsrc_t rC =
+            make_rsrc(C + (size_t)m0 * N + n0, ((int64_t)(M - m0) * N - n0) * 2);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-        const int ml = wm * 128 + mi * 32 + (lane & 31);
-        const bool mvalid = (m0 + ml) < M;
+        for (int mi = 0; mi < 4; ++mi) {
+            const int ml = wm * 128 + mi * 32 + (lane & 31);
+            const bool mvalid = (m0 + ml) < M;
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
+            for (int ni = 0; ni < 4; ++ni) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int nl = wn * 128 + ni * 32 + 8 * g + 4 * (lane >> 5);
-                const bool ok = mvalid && (n0 + nl) < N;
-                const uint32_t off = ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 2u : kOOB;
-                const f32x16_t& a = acc[mi][ni];
-                store8(rC, off, pack_bf16x4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]));
+                for (int g = 0; g < 4; ++g) {
+                    const int nl = wn * 128 + ni * 32 + 8 * g + 4 * (lane >> 5);
+                    const bool ok = mvalid && (n0 + nl) < N;
+                    const uint32_t off =
+                        ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 2u : kOOB;
+                    const f32x16_t& a = acc[mi][ni];
+                    store8(rC, off,
+                           pack_bf16x4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]));
+                }
+            }
+        }
+    } else {
+        float* wsb = ws + ((size_t)blockIdx.y * M + m0) * N + n0;
+        const __amdgpu_buffer_rsrc_t rW = make_rsrc(wsb, ((int64_t)(M - m0) * N - n0) * 4);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            const int ml = wm * 128 + mi * 32 + (lane & 31);
+            const bool mvalid = (m0 + ml) < M;
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int nl = wn * 128 + ni * 32 + 8 * g + 4 * (lane >> 5);
+                    const bool ok = mvalid && (n0 + nl) < N;
+                    const uint32_t off =
+                        ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 4u : kOOB;
+                    const f32x16_t& a = acc[mi][ni];
+                    const f32x4_t v = {a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+                    store16(rW, off, __builtin_bit_cast(u32x4_t, v));
+                }
             }
         }
     }
@@ -882,6 +927,31 @@ int env_int(const char* name, int dflt) {
     return (v && *v) ? std::atoi(v) : dflt;
 }
 
+// K splits for the tile kernel from a cost model, in microseconds, measured on MI355X: a 32-deep
+// K step of a 256x256 tile takes about 0.85 us on one CU; with splits, the fp32 partials are
+// written and read back at about 3.5 TB/s and the reduction launch adds about 4 us. Time of s
+// splits = waves * steps per split * 0.85 (+ partial traffic + 4 if s > 1); the smallest wins,
+// ties to fewer splits. With at least as many tiles as CUs this is always 1.
+int choose_splits(int64_t M, int64_t N, int64_t K, int tiles, int n_cu, int max_splits) {
+    constexpr double kStepUs = 0.85, kPartialBytesPerUs = 3.5e6, kReduceLaunchUs = 4.0;
+    int best = 1;
+    double best_t = 0.0;
+    for (int s = 1; s <= max_splits; ++s) {
+        int64_t kps = (K + s - 1) / s;
+        kps = (kps + td::BK - 1) / td::BK * td::BK;
+        const int64_t splits = (K + kps - 1) / kps;
+        if (splits != s) continue;  // the same split as a smaller s
+        const int64_t waves = ((int64_t)tiles * s + n_cu - 1) / n_cu;
+        double t = (double)waves * (double)(kps / td::BK) * kStepUs;
+        if (s > 1) t += kReduceLaunchUs + (double)s * (double)M * (double)N * 8.0 / kPartialBytesPerUs;
+        if (s == 1 || t < best_t) {
+            best = s;
+            best_t = t;
+        }
+    }
+    return best;
+}
+
 }  // namespace
 
 namespace c3 {
@@ -947,6 +1017,36 @@ c3_status gemm_plan(const void* A, const void* B, void* C, int64_t M, int64_t N,
         }
     } else {
         p.kind = 0;
+#if C3_GEMM_KERNEL == 1
+        // Fewer output tiles than CUs: K may be split too, so that more of the chip works
+        // (each split keeps at least 4 K steps so that the LDS pipeline fills); fp32 partials
+        // are summed in split order by splitk_reduce. The count follows the device's CU count,
+        // never a stream's CU mask, so C is the same under any mask.
+        const int tiles = ((p.M + td::BM - 1) / td::BM) * ((p.N + td::BN - 1) / td::BN);
+        const int n_cu = ctx().info.n_cu > 0 ? ctx().info.n_cu : 256;
+        const int max_splits = std::max(1, std::min(256, (int)(K / (4 * td::BK))));
+        int splits = env_int("C3_GEMM_SPLITS", 0);
+        if (splits <= 0) splits = choose_splits(M, N, K, tiles, n_cu, max_splits);
+        splits = std::max(1, std::min(splits, max_splits));
+        int kps = (int)((K + splits - 1) / splits);
+        kps = (kps + td::BK - 1) / td::BK * td::BK;
+        splits = (int)((K + kps - 1) / kps);
+        p.splits = splits;
+        p.k_per_split = splits > 1 ? kps : (int)K;
+        if (splits > 1) {
+            const size_t need = (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
+            Workspace& w = workspaces()[stream];
+            if (w.bytes < need) {
+                if (w.ptr) C3_HIP_TRY(hipFree(w.ptr));
+                w.ptr = nullptr;
+                w.bytes = 0;
+                C3_HIP_TRY(hipMalloc(&w.ptr, need));
+                w.bytes = need;
+            }
+            p.workspace = w.ptr;
+            p.workspace_bytes = need;
+        }
+#endif
     }
     *plan = p;
     return C3_OK;
@@ -959,12 +1059,21 @@ c3_status gemm_enqueue(const GemmPlan& p, hipStream_t stream) {
     if (p.kind == 0) {
         const int tiles_m = (p.M + t256::BM - 1) / t256::BM;
         const int tiles_n = (p.N + t256::BN - 1) / t256::BN;
-#ifndef C3_GEMM_KERNEL
-#define C3_GEMM_KERNEL 1
-#endif
 #if C3_GEMM_KERNEL == 1
-        hipLaunchKernelGGL(gemm_bf16_tile256_dma, dim3(tiles_m * tiles_n), dim3(td::NT), 0, stream,
-                           A, B, C, p.M, p.N, p.K, tiles_m, tiles_n);
+        if (p.splits > 1 && !p.workspace) return fail(C3_E_INVALID, "split-K plan without workspace");
+        if (p.splits > 1)
+            hipLaunchKernelGGL(gemm_bf16_tile256_dma<true>, dim3(tiles_m * tiles_n, p.splits),
+                               dim3(td::NT), 0, stream, A, B, C, p.workspace, p.M, p.N, p.K,
+                               p.k_per_split, tiles_m, tiles_n);
+        else
+            hipLaunchKernelGGL(gemm_bf16_tile256_dma<false>, dim3(tiles_m * tiles_n), dim3(td::NT),
+                               0, stream, A, B, C, nullptr, p.M, p.N, p.K, p.K, tiles_m, tiles_n);
+        C3_HIP_TRY(hipGetLastError());
+        if (p.splits > 1) {
+            const int64_t quads = (int64_t)p.M * (p.N / 4);
+            hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0,
+                               stream, p.workspace, C, p.M, p.N, p.M, p.splits);
+        }
 #else
         hipLaunchKernelGGL(gemm_bf16_tile256, dim3(tiles_m * tiles_n), dim3(t256::NT), 0, stream,
                            A, B, C, p.M, p.N, p.K, tiles_m, tiles_n);

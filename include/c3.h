@@ -257,6 +257,10 @@ c3_status c3_probe_placement(void* stream, int n_blocks, uint32_t* out_dev);
  * fp32 accumulation; C is overwritten with the sum rounded to nearest-even bf16 (no alpha,
  * beta, bias). Deterministic: no atomics, fixed reduction order, same bits on every run and
  * under any CU mask. Stream-ordered and asynchronous. A/B must not overlap C (C3_E_OVERLAP).
+ * M <= 64, and shapes with fewer 256x256 output tiles than CUs where a cost model says it pays,
+ * split K over workgroups: fp32 partials in a workspace the library allocates per stream on first
+ * need (kept until c3_finalize), summed in split order. The split count depends only on the
+ * shape and the device, so the bits do not change between calls.
  * GEMM kernels of LLaMA-70B/405B training are the paper's computation (Section IV, Fig. 5a). */
 c3_status c3_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                   void* stream);

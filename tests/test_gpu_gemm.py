@@ -13,8 +13,8 @@ from gpu_util import bf16_from_dev, empty_bf16, to_dev
 
 pytestmark = pytest.mark.gpu
 
-# (M, N, K): several 256x256x64 tiles with ragged tails, skinny shapes (M <= 64) with ragged N
-# and K, and single-element edges.
+# (M, N, K): several 256x256 tiles with ragged tails (with fewer tiles than CUs, K is split too),
+# skinny shapes (M <= 64) with ragged N and K, and single-element edges.
 SHAPES = [
     (1, 8, 8), (3, 24, 40), (16, 264, 136), (17, 520, 328), (33, 1000, 64), (64, 256, 512),
     (64, 8, 2048), (65, 256, 64), (300, 264, 72), (256, 256, 64), (512, 512, 512),
@@ -102,6 +102,28 @@ def test_gemm_deterministic_and_mask_invariant(c3gpu):
     A2 = wl.gen_bf16((16, 8192), ("normal", 0.0, 1.0), 7902)
     B2 = wl.gen_bf16((8192, 1032), ("normal", 0.0, 0.02), 7903)
     np.testing.assert_array_equal(run_gemm(c3gpu, A2, B2), run_gemm(c3gpu, A2, B2))
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 1024, 4096), (300, 520, 1040), (512, 768, 4096),
+                                   (200, 264, 1000)])
+def test_gemm_split_k(c3gpu, M, N, K, monkeypatch):
+    """Fewer 256x256 tiles than CUs: K is split over workgroups (fp32 partials summed in split
+    order). Split and unsplit (C3_GEMM_SPLITS=1) results both meet the bar against the oracle,
+    and the split result is the same on every run."""
+    print(f"split-K GEMM {M}x{N}x{K}", flush=True)
+    A = wl.gen_bf16((M, K), ("normal", 0.0, 1.0), 7950 + M)
+    B = wl.gen_bf16((K, N), ("normal", 0.0, 0.02), 7951 + N)
+    ref = oracle.gemm_f64acc(A, B)
+    split = run_gemm(c3gpu, A, B)
+    check_tol(ref, split)
+    np.testing.assert_array_equal(split, run_gemm(c3gpu, A, B))
+    monkeypatch.setenv("C3_GEMM_SPLITS", "1")
+    check_tol(ref, run_gemm(c3gpu, A, B))
+    # integer-exact operands: every partial sum is exact, so the split sum is too
+    monkeypatch.delenv("C3_GEMM_SPLITS")
+    Ai = wl.gen_small_int_bf16((M, K), 7960 + K)
+    Bi = wl.gen_small_int_bf16((K, N), 7961 + N)
+    np.testing.assert_array_equal(run_gemm(c3gpu, Ai, Bi), oracle.gemm_f32acc(Ai, Bi))
 
 
 def test_gemm_argument_errors(c3gpu):
