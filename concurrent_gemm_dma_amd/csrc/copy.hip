@@ -21,13 +21,8 @@ constexpr int kThreads = 256;
 // One piece per lane per pass and 8 KiB per workgroup measured fastest on MI355X (6.27 TB/s of
 // read + write for a 1 GiB gather; 5.9 TB/s for 4 pieces and 32 KiB, 5.5 TB/s for 8 and 64 KiB):
 // many small workgroups keep more requests in flight across the chip than few long ones.
-#ifndef C3_COPY_UNROLL
-#define C3_COPY_UNROLL 1
-#endif
-#ifndef C3_COPY_BLOCK_KIB
-#define C3_COPY_BLOCK_KIB 8
-#endif
-constexpr int kUnroll = C3_COPY_UNROLL;
+constexpr int kUnroll = 1;           // 16-byte pieces per lane per pass
+constexpr uint64_t kBlockKiB = 8;      // payload per workgroup
 constexpr uint64_t kPiecesPerIter = (uint64_t)kThreads * kUnroll;  // 16-byte pieces
 
 struct SegTable {
@@ -175,7 +170,7 @@ c3_status copy_cu_enqueue(const std::vector<Segment>& segs, const c3_move_opts& 
             per_block = (acc + blocks - 1) / blocks;
             per_block = (per_block + kPiecesPerIter - 1) / kPiecesPerIter * kPiecesPerIter;
         } else {
-            per_block = (uint64_t)C3_COPY_BLOCK_KIB * 64;  // 16-byte pieces per workgroup
+            per_block = kBlockKiB * 64;  // 16-byte pieces per workgroup
         }
         blocks = (acc + per_block - 1) / per_block;
         if (blocks > 0x7FFFFFFFull) return fail(C3_E_INVALID, "copy too large for one launch");

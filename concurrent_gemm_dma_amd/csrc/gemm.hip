@@ -4,13 +4,14 @@
 // The paper's computation is the GEMM of LLaMA-class training layers ("Optimizing ML Concurrent
 // Computation and Communication with GPU DMA Engines", Section IV, Fig. 5a). Two kernels:
 //
-// * tile256: 256x256 output tile per workgroup, K step 64, 4 waves (2x2), each wave 128x128
-//   built from 4x4 v_mfma_f32_32x32x16_bf16. Operands are staged global -> registers -> LDS
-//   (double-buffered, one barrier per K step). The MFMA is fed transposed (B^T as the row
-//   operand, A^T as the column operand), so each lane's accumulators are 4 consecutive columns
-//   of one C row and the epilogue writes 8-byte runs. B stays K x N in LDS and is read with the
-//   LDS transpose load (ds_read_b64_tr_b16), which hands each lane 4 consecutive k of one
-//   column. Compute-bound shapes use this kernel.
+// * tile256_dma: 256x256 output tile per workgroup, 4 waves (2x2), each wave 128x128 built from
+//   4x4 v_mfma_f32_32x32x16_bf16. Operands go global -> LDS directly (LDS-direct buffer loads),
+//   K step 32, four LDS stages. The MFMA is fed transposed (B^T as the row operand, A^T as the
+//   column operand), so each lane's accumulators are 4 consecutive columns of one C row and the
+//   epilogue writes 8-byte runs. B stays K x N in LDS and is read with the LDS transpose load
+//   (ds_read_b64_tr_b16), which hands each lane 4 consecutive k of one column. With fewer tiles
+//   than CUs, K can also be split over a second grid dimension (fp32 partials, summed in split
+//   order by splitk_reduce). Every shape with M > 64 uses this kernel.
 // * skinny: all M (<= 64) rows x 256 columns per workgroup, K split across workgroups
 //   (deterministic: fp32 partials per split, summed in split order by a second kernel),
 //   v_mfma_f32_16x16x32_bf16. For M <= 64, where the GEMM streams B once and is bound by HBM
@@ -25,12 +26,6 @@
 #include <cstdlib>
 #include <map>
 #include <type_traits>
-
-// 1 = the LDS-direct 256x256 tile kernel (with split-K for small tile counts); 0 = the earlier
-// register-staged tile kernel (no split-K), kept for comparison.
-#ifndef C3_GEMM_KERNEL
-#define C3_GEMM_KERNEL 1
-#endif
 
 namespace {
 
@@ -131,203 +126,6 @@ __device__ __forceinline__ void map_tile(int bid, int nblocks, int tiles_m, int 
 }
 
 // ------------------------------------------------------------------------------------------------
-// 256 x 256 tile kernel
-// ------------------------------------------------------------------------------------------------
-namespace t256 {
-constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
-constexpr int A_STAGE = BM * BK * 2;  // 32 KiB
-constexpr int B_STAGE = BK * BN * 2;  // 32 KiB
-constexpr int STAGE = A_STAGE + B_STAGE;
-constexpr int A_LD = BM * BK / 8 / NT;  // 16-byte chunks per thread per stage: 8
-constexpr int B_LD = BK * BN / 8 / NT;  // 8
-constexpr int GROUP_M = 8;
-}  // namespace t256
-
-__global__ __launch_bounds__(256, 1) void gemm_bf16_tile256(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
-    int M, int N, int K, int tiles_m, int tiles_n) {
-    using namespace t256;
-    __shared__ __attribute__((aligned(128))) char smem[2 * STAGE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    int tm, tn;
-    map_tile<GROUP_M>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-
-    // ---- global -> register addressing (per thread: 8 A chunks, 8 B chunks per stage) ----
-    // A chunk i of this thread: row i*32 + tid/8, k chunk tid%8.
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(A + (size_t)m0 * K, (int64_t)(M - m0) * K * 2);
-    const int a_row = tid >> 3, a_kc = tid & 7;
-    const uint32_t a_g0 = (uint32_t)a_row * (uint32_t)K * 2u + (uint32_t)a_kc * 16u;
-    const uint32_t a_gstep = 32u * (uint32_t)K * 2u;
-    const uint32_t a_s0 = (uint32_t)a_row * 128u + (uint32_t)((a_kc ^ swz_a(a_row)) << 4);
-    // B chunk i of this thread: k row i*8 + tid/32, n chunk tid%32.
-    const int b_row = tid >> 5, b_nc = tid & 31;
-    const bool b_nvalid = (n0 + b_nc * 8) < N;
-    const uint32_t b_g0 = (uint32_t)b_row * (uint32_t)N * 2u + (uint32_t)b_nc * 16u;
-    const uint32_t b_gstep = 8u * (uint32_t)N * 2u;
-    const uint32_t b_s0 = (uint32_t)b_row * 512u + (uint32_t)((b_nc ^ swz_b(b_row)) << 4);
-
-    // ---- LDS -> MFMA operand addressing ----
-    // Column operand (A^T): lane reads row wm*128 + mi*32 + lane%32, k chunk kk*2 + lane/32.
-    const int ar = lane & 31;
-    const int a_sw = swz_a(ar);  // bits 0..3 of the row equal those of lane%32
-    uint32_t a_rd[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-        a_rd[kk] = (uint32_t)(wm * 128 + ar) * 128u +
-                   (uint32_t)((((kk * 2) + (lane >> 5)) ^ a_sw) << 4);
-    // Row operand (B^T) via transpose loads: lane (group G = lane/16, p = lane%16) supplies
-    // 4 n-contiguous bf16 of k row 8*(G/2) + p/4 (+16*kk, +4*h) at n = 32*ni + 16*(G%2) + 4*(p%4)
-    // of this wave's 128 columns; the load hands lane p column p of that 4 x 16 block.
-    const int G = lane >> 4, p = lane & 15;
-    const int b_krow = 8 * (G >> 1) + (p >> 2);
-    const int b_sw = swz_b(p >> 2);
-    uint32_t b_rd[4];
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-        const int nc = wn * 16 + ni * 4 + 2 * (G & 1) + ((p >> 1) & 1);
-        b_rd[ni] = (uint32_t)b_krow * 512u + (uint32_t)((nc ^ b_sw) << 4) + (uint32_t)((p & 1) * 8);
-    }
-
-    f32x16_t acc[4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x16_t{};
-
-    u32x4_t ra[A_LD], rb[B_LD];
-
-    auto load_regs = [&](int k0, u32x4_t* xa, u32x4_t* xb) {
-        const bool a_kvalid = (k0 + a_kc * 8) < K;
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i)
-            xa[i] = load16(rA, a_kvalid ? a_g0 + (uint32_t)i * a_gstep + (uint32_t)k0 * 2u : kOOB);
-        const __amdgpu_buffer_rsrc_t rB =
-            make_rsrc(B + (size_t)k0 * N + n0, ((int64_t)(K - k0) * N - n0) * 2);
-#pragma unroll
-        for (int i = 0; i < B_LD; ++i)
-            xb[i] = load16(rB, b_nvalid ? b_g0 + (uint32_t)i * b_gstep : kOOB);
-    };
-    auto store_regs = [&](int s, const u32x4_t* xa, const u32x4_t* xb) {
-        char* As = smem + s * STAGE;
-        char* Bs = As + A_STAGE;
-#pragma unroll
-        for (int i = 0; i < A_LD; ++i) lds_store16(As, a_s0 + (uint32_t)i * 4096u, xa[i]);
-#pragma unroll
-        for (int i = 0; i < B_LD; ++i) lds_store16(Bs, b_s0 + (uint32_t)i * 4096u, xb[i]);
-    };
-    auto load_stage = [&](int k0) { load_regs(k0, ra, rb); };
-    auto store_stage = [&](int s) { store_regs(s, ra, rb); };
-#ifndef C3_GEMM_PIPE
-#define C3_GEMM_PIPE 1
-#endif
-    auto load_frags = [&](const char* As, const char* Bs, int kk, bf16x8_t* colop,
-                          bf16x8_t* rowop) {
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) colop[mi] = lds_load16(As, a_rd[kk] + mi * 4096u);
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-            rowop[ni] = lds_load_tr8(Bs, b_rd[ni] + kk * 8192u, b_rd[ni] + kk * 8192u + 2048u);
-    };
-    auto mfma_block = [&](const bf16x8_t* colop, const bf16x8_t* rowop) {
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowop[ni], colop[mi],
-                                                                      acc[mi][ni], 0, 0, 0);
-    };
-    auto compute_stage = [&](int s) {
-        const char* As = smem + s * STAGE;
-        const char* Bs = As + A_STAGE;
-#if C3_GEMM_PIPE
-        // Operand fragments double-buffered in registers: the 12 LDS reads of step kk+1 are
-        // issued before the 16 MFMAs of step kk (scheduling barriers keep that order), so the
-        // reads complete under the MFMAs instead of stalling them.
-        bf16x8_t colop[2][4], rowop[2][4];
-        load_frags(As, Bs, 0, colop[0], rowop[0]);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            if (kk < 3) load_frags(As, Bs, kk + 1, colop[(kk + 1) & 1], rowop[(kk + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_block(colop[kk & 1], rowop[kk & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#else
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            bf16x8_t colop[4], rowop[4];
-            load_frags(As, Bs, kk, colop, rowop);
-            mfma_block(colop, rowop);
-        }
-#endif
-    };
-
-    const int nk = (K + BK - 1) / BK;
-#ifndef C3_GEMM_PREFETCH2
-#define C3_GEMM_PREFETCH2 0
-#endif
-#if C3_GEMM_PREFETCH2
-    // Global loads run two K steps ahead in two register sets (the loop is unrolled by two so
-    // each set is named statically): the loads of step k+2 are issued before step k is
-    // computed and written to LDS only at the end of step k+1, giving them two steps of MFMA
-    // work to arrive. LDS stays double-buffered with one barrier per step.
-    u32x4_t ra1[A_LD], rb1[B_LD];
-    load_regs(0, ra, rb);
-    if (nk > 1) load_regs(BK, ra1, rb1);
-    store_regs(0, ra, rb);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-        if (kt + 2 < nk) load_regs((kt + 2) * BK, ra, rb);
-        compute_stage(0);
-        if (kt + 1 < nk) store_regs(1, ra1, rb1);
-        __syncthreads();
-        if (kt + 1 >= nk) break;
-        if (kt + 3 < nk) load_regs((kt + 3) * BK, ra1, rb1);
-        compute_stage(1);
-        if (kt + 2 < nk) store_regs(0, ra, rb);
-        __syncthreads();
-    }
-#else
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) load_stage((kt + 1) * BK);
-        compute_stage(cur);
-        if (kt + 1 < nk) store_stage(cur ^ 1);
-        __syncthreads();
-    }
-#endif
-
-    // ---- epilogue: lane holds C[m][n..n+3], m = mi*32 + lane%32, n = ni*32 + 8g + 4*(lane/32)
-    const __amdgpu_buffer_rsrc_t rC =
-        make_rsrc(C + (size_t)m0 * N + n0, ((int64_t)(M - m0) * N - n0) * 2);
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-        const int ml = wm * 128 + mi * 32 + (lane & 31);
-        const bool mvalid = (m0 + ml) < M;
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int nl = wn * 128 + ni * 32 + 8 * g + 4 * (lane >> 5);
-                const bool ok = mvalid && (n0 + nl) < N;
-                const uint32_t off = ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 2u : kOOB;
-                const f32x16_t& a = acc[mi][ni];
-                store8(rC, off, pack_bf16x4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]));
-            }
-        }
-    }
-}
-
-// ------------------------------------------------------------------------------------------------
 // 256 x 256 tile kernel, LDS-direct loads
 // ------------------------------------------------------------------------------------------------
 // Same tile, waves and MFMA layout as above, but operands go global -> LDS directly
@@ -342,10 +140,7 @@ constexpr int BM = 256, BN = 256, BK = 32, NT = 256, NSTAGE = 4;
 constexpr int A_STAGE = BM * BK * 2;  // 16 KiB: 256 rows of 64 B
 constexpr int B_STAGE = BK * BN * 2;  // 16 KiB: 32 rows of 512 B
 constexpr int STAGE = A_STAGE + B_STAGE;
-#ifndef C3_GEMM_GROUP_M
-#define C3_GEMM_GROUP_M 4
-#endif
-constexpr int GROUP_M = C3_GEMM_GROUP_M;
+constexpr int GROUP_M = 4;            // tile rows walked together on one XCD (map_tile)
 constexpr int LOADS_PER_STAGE = 8;    // per wave: 4 A + 4 B wave-instructions
 }  // namespace td
 
@@ -475,32 +270,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x16_t{};
 
-    auto load_frags = [&](int s, int kk, bf16x8_t* colop, bf16x8_t* rowop) {
-        const char* As = smem + s * STAGE;
-        const char* Bs = As + A_STAGE;
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) colop[mi] = lds_load16(As, a_rd[kk] + mi * 2048u);
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-            rowop[ni] = lds_load_tr8(Bs, b_rd[ni] + kk * 8192u, b_rd[ni] + kk * 8192u + 2048u);
-    };
-    auto mfma_block = [&](const bf16x8_t* colop, const bf16x8_t* rowop) {
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowop[ni], colop[mi],
-                                                                      acc[mi][ni], 0, 0, 0);
-    };
-
     const int nk = (Ke + BK - 1) / BK;
-#ifndef C3_GEMM_INTERLEAVE
-#define C3_GEMM_INTERLEAVE 1
-#endif
-#ifndef C3_GEMM_DMA_SPLIT
-#define C3_GEMM_DMA_SPLIT 1
-#endif
-#if C3_GEMM_INTERLEAVE && C3_GEMM_DMA_SPLIT
     // Split refill: a stage's A half is issued one half-step earlier than its B half, so the
     // prologue issues stages 0..2 whole and only the A half of stage 3.
 #pragma unroll
@@ -519,18 +289,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     else if (nk == 3) C3_WAIT_VMCNT(4 * 4);
     else if (nk == 2) C3_WAIT_VMCNT(2 * 4);
     else C3_WAIT_VMCNT(0);
-#else
-#pragma unroll
-    for (int s = 0; s < NSTAGE; ++s)
-        if (s < nk) issue_stage(s * BK, s);
-    if (nk >= 4) C3_WAIT_VMCNT(3 * LOADS_PER_STAGE);
-    else if (nk == 3) C3_WAIT_VMCNT(2 * LOADS_PER_STAGE);
-    else if (nk == 2) C3_WAIT_VMCNT(1 * LOADS_PER_STAGE);
-    else C3_WAIT_VMCNT(0);
-#endif
     __syncthreads();
 
-#if C3_GEMM_INTERLEAVE
     // With one wave per SIMD the MFMA pipe idles whenever the wave issues anything else between
     // two MFMAs, so every other instruction is slotted one-for-one behind an MFMA (scheduling
     // fences after each slot keep this order): while an MFMA occupies the pipe for its 32
@@ -569,12 +329,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     //   BA - first half issues the B half of step kt+3 into buffer (kt+3)%4 (split refill; that
     //        buffer's last reader, step kt-1, finished before the previous step's barrier),
     //   RA - second half issues the A half of step kt+4 into this step's buffer,
-    //   RB - second half issues the B half of step kt+4 too (whole refill),
     //   NX - second half reads step kt+1's first fragments.
-    auto step = [&](int kt, auto ba_c, auto ra_c, auto rb_c, auto nx_c) {
+    auto step = [&](int kt, auto ba_c, auto ra_c, auto nx_c) {
         constexpr bool BA = decltype(ba_c)::value;
         constexpr bool RA = decltype(ra_c)::value;
-        constexpr bool RB = decltype(rb_c)::value;
         constexpr bool NX = decltype(nx_c)::value;
         const int s = kt & (NSTAGE - 1);
         const int s3 = (kt + NSTAGE - 1) & (NSTAGE - 1);
@@ -604,10 +362,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         const int s1 = (kt + 1) & (NSTAGE - 1);
         const int k0 = (kt + NSTAGE) * BK;
         const bool a_ok = (k0 + a_kc * 8) < Ke;
-        i32x4_t rB{};
-        if (RB) rB = make_rsrc_words(B + (size_t)k0 * N + n0, ((int64_t)(Ke - k0) * N - n0) * 2);
         const uint32_t a_dst = a_dst0 + (uint32_t)s * STAGE;
-        const uint32_t b_dst = b_dst0 + (uint32_t)s * STAGE;
         const uint32_t a_off = a_g0 + (uint32_t)k0 * 2u;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -615,8 +370,6 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
             if (NX && i < 12) read_item(s1, 0, 0, i);
             if (RA && i < 4)
                 lds_dma16_at(rA, a_dst + i * 1024u, a_ok ? a_off + (uint32_t)i * a_gstep : kOOB);
-            if (RB && i >= 4 && i < 8)
-                lds_dma16_at(rB, b_dst + (i - 4) * 1024u, b_ok[i - 4] ? b_g[i - 4] : kOOB);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -626,39 +379,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
 #pragma unroll
     for (int j = 0; j < 12; ++j) read_item(0, 0, 0, j);
     int kt = 0;
-#if C3_GEMM_DMA_SPLIT
-    for (; kt + NSTAGE < nk; ++kt) step(kt, T{}, T{}, F{}, T{});
+    for (; kt + NSTAGE < nk; ++kt) step(kt, T{}, T{}, T{});
     if (kt + NSTAGE - 1 < nk) {
-        step(kt, T{}, F{}, F{}, T{});
+        step(kt, T{}, F{}, T{});
         ++kt;
     }
-#else
-    for (; kt + NSTAGE < nk; ++kt) step(kt, F{}, T{}, T{}, T{});
-#endif
-    for (; kt + 1 < nk; ++kt) step(kt, F{}, F{}, F{}, T{});
-    if (kt < nk) step(kt, F{}, F{}, F{}, F{});
-#else
-    bf16x8_t c0[4], r0[4], c1[4], r1[4];
-    load_frags(0, 0, c0, r0);
-    for (int kt = 0; kt < nk; ++kt) {
-        const int s = kt & (NSTAGE - 1);
-        load_frags(s, 1, c1, r1);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_block(c0, r0);
-        __builtin_amdgcn_sched_barrier(0);
-        // step kt+1 landed for this wave; stages kt+2, kt+3 may still be in flight
-        if (kt + 3 < nk) C3_WAIT_VMCNT(2 * LOADS_PER_STAGE);
-        else if (kt + 2 < nk) C3_WAIT_VMCNT(1 * LOADS_PER_STAGE);
-        else C3_WAIT_VMCNT(0);
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of step kt are done
-        __syncthreads();
-        if (kt + NSTAGE < nk) issue_stage((kt + NSTAGE) * BK, s);
-        if (kt + 1 < nk) load_frags((kt + 1) & (NSTAGE - 1), 0, c0, r0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_block(c1, r1);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-#endif
+    for (; kt + 1 < nk; ++kt) step(kt, F{}, F{}, T{});
+    if (kt < nk) step(kt, F{}, F{}, F{});
 
     // ---- epilogue: lane holds C[m][n..n+3], m = mi*32 + lane%32, n = ni*32 + 8g + 4*(lane/32);
     // one K split writes bf16 C, several write fp32 partials ws[y][m][n] for splitk_reduce
@@ -787,13 +514,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_skinny(
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) acc[mt][ni] = f32x4_t{};
 
-#ifndef C3_SKINNY_PF
-#define C3_SKINNY_PF 1
-#endif
-    // Register staging sets: with two, the loads run two K steps ahead of the MFMAs. One is the
-    // default: two measured no faster (85-160 us either way for the skinny workloads), so bytes
+    // Register staging sets: with two, the loads would run two K steps ahead of the MFMAs. One
+    // is used: two measured no faster (85-160 us either way for the skinny workloads), so bytes
     // in flight are not what limits this stream.
-    constexpr int PF = C3_SKINNY_PF;
+    constexpr int PF = 1;
     u32x4_t ra[PF][A_LD], rb[PF][B_LD];
     auto load_stage = [&](int k0, int set) {
 #pragma unroll
@@ -1017,7 +741,6 @@ c3_status gemm_plan(const void* A, const void* B, void* C, int64_t M, int64_t N,
         }
     } else {
         p.kind = 0;
-#if C3_GEMM_KERNEL == 1
         // Fewer output tiles than CUs: K may be split too, so that more of the chip works
         // (each split keeps at least 4 K steps so that the LDS pipeline fills); fp32 partials
         // are summed in split order by splitk_reduce. The count follows the device's CU count,
@@ -1046,7 +769,6 @@ c3_status gemm_plan(const void* A, const void* B, void* C, int64_t M, int64_t N,
             p.workspace = w.ptr;
             p.workspace_bytes = need;
         }
-#endif
     }
     *plan = p;
     return C3_OK;
@@ -1057,9 +779,8 @@ c3_status gemm_enqueue(const GemmPlan& p, hipStream_t stream) {
     const auto* B = static_cast<const uint16_t*>(p.B);
     auto* C = static_cast<uint16_t*>(p.C);
     if (p.kind == 0) {
-        const int tiles_m = (p.M + t256::BM - 1) / t256::BM;
-        const int tiles_n = (p.N + t256::BN - 1) / t256::BN;
-#if C3_GEMM_KERNEL == 1
+        const int tiles_m = (p.M + td::BM - 1) / td::BM;
+        const int tiles_n = (p.N + td::BN - 1) / td::BN;
         if (p.splits > 1 && !p.workspace) return fail(C3_E_INVALID, "split-K plan without workspace");
         if (p.splits > 1)
             hipLaunchKernelGGL(gemm_bf16_tile256_dma<true>, dim3(tiles_m * tiles_n, p.splits),
@@ -1074,10 +795,6 @@ c3_status gemm_enqueue(const GemmPlan& p, hipStream_t stream) {
             hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0,
                                stream, p.workspace, C, p.M, p.N, p.M, p.splits);
         }
-#else
-        hipLaunchKernelGGL(gemm_bf16_tile256, dim3(tiles_m * tiles_n), dim3(t256::NT), 0, stream,
-                           A, B, C, p.M, p.N, p.K, tiles_m, tiles_n);
-#endif
         C3_HIP_TRY(hipGetLastError());
         return C3_OK;
     }

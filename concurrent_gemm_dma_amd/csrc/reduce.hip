@@ -43,21 +43,12 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return __builtin_bit_cast(uint32_t, p);
 }
 
-#ifndef C3_REDUCE_PIECES
-#define C3_REDUCE_PIECES 1
-#endif
-#ifndef C3_REDUCE_NT
-#define C3_REDUCE_NT 1
-#endif
 // One piece per lane and streaming (non-temporal) loads and stores measured fastest on MI355X:
 // 8 ranks x 32 MiB in 51.8 us = 5.83 TB/s of (world + 1) * chunk bytes; 2 or 4 pieces per lane
-// were 4% and 35% slower (fewer, longer workgroups).
-constexpr int kPieces = C3_REDUCE_PIECES;  // 16-byte pieces per lane
+// were 4% and 35% slower (fewer, longer workgroups), ordinary loads and stores 11% slower.
+constexpr int kPieces = 1;  // 16-byte pieces per lane
 
-__device__ __forceinline__ u32x4_t load16(const u32x4_t* p) {
-    if (C3_REDUCE_NT) return __builtin_nontemporal_load(p);
-    return *p;
-}
+__device__ __forceinline__ u32x4_t load16(const u32x4_t* p) { return __builtin_nontemporal_load(p); }
 
 // Workgroup b owns pieces [b * kPieces * kThreads, (b + 1) * kPieces * kThreads); lane t takes
 // pieces t, t + kThreads, ... of that range (each access coalesced across the wavefront).
@@ -100,8 +91,7 @@ __global__ __launch_bounds__(kThreads) void reduce_sum_vec(const InTable t, int 
             u32x4_t o;
 #pragma unroll
             for (int h = 0; h < 4; ++h) o[h] = pack2(acc[q][2 * h], acc[q][2 * h + 1]);
-            if (C3_REDUCE_NT) __builtin_nontemporal_store(o, out + i);
-            else out[i] = o;
+            __builtin_nontemporal_store(o, out + i);
         }
     }
 }
