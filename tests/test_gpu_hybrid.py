@@ -161,3 +161,41 @@ def test_hybrid_concurrent_allreduce(c3gpu):
     t = c3gpu.c3_run_concurrent(None, cargs, c3gpu.conc_opts(flush_bytes=64 * MiB))
     case.check_comm("isolated hybrid all-reduce")
     assert t["t_gemm_done_ns"] == 0 and t["t_copy_done_ns"] > 0 and t["reduce_gpu_ms"] > 0
+
+
+def test_hybrid_fault_hooks(c3gpu):
+    """Host-forced SDMA faults in the engines' share: a dropped transfer leaves exactly its bytes
+    stale (the CU share is intact, the byte check catches it); a stuck or failed transfer is
+    reported, alone and beside a GEMM, after the CU share finished; the library stays usable."""
+    sb = 256 * KiB
+    shards = [wl.gen_bytes(sb, 12900 + i) for i in range(8)]
+    want = oracle.gather(shards)
+    # 500 per mille with 128 KiB chunks: engine chunk i is the first half of shard i
+    got, _ = gather(c3gpu, shards, hybrid(c3gpu, 500, chunk_bytes=128 * KiB,
+                                          fault_mode=c3gpu.C3_FAULT_DROP_CHUNK, fault_chunk=3))
+    off = oracle.first_diff(want, got)
+    assert 3 * sb <= off < 3 * sb + sb // 2
+    assert oracle.first_diff(want[3 * sb + sb // 2:], got[3 * sb + sb // 2:]) == -1
+    with pytest.raises(c3gpu.C3Error) as e:
+        gather(c3gpu, shards, hybrid(c3gpu, 500, chunk_bytes=128 * KiB, timeout_ms=300,
+                                     fault_mode=c3gpu.C3_FAULT_STUCK_CHUNK, fault_chunk=5))
+    assert e.value.status == c3gpu.C3_E_TIMEOUT
+    # beside a GEMM: the error comes back after both operations finished, C is still right
+    case = Case(c3gpu, 512, 512, 512, "gather", 8, sb, 12950)
+    case.poison(0)
+    c3gpu.c3_run_concurrent(case.gargs(c3gpu), None)
+    iso_c = bf16_from_dev(case.dC)
+    case.poison(1)
+    cargs, _keep = case.cargs(c3gpu, c3gpu.C3_MOVER_HYBRID,
+                              hybrid(c3gpu, 500, chunk_bytes=128 * KiB,
+                                     fault_mode=c3gpu.C3_FAULT_ERROR_CHUNK, fault_chunk=0))
+    with pytest.raises(c3gpu.C3Error) as e:
+        c3gpu.c3_run_concurrent(case.gargs(c3gpu), cargs, c3gpu.conc_opts(comm_first=True))
+    assert e.value.status == c3gpu.C3_E_HSA
+    np.testing.assert_array_equal(bf16_from_dev(case.dC), iso_c)
+    got = bytes_from_dev(case.dst)
+    for i in range(8):  # every CU share (second halves) landed
+        lo = i * sb + sb // 2
+        assert oracle.first_diff(case.want[lo:lo + sb // 2], got[lo:lo + sb // 2]) == -1, i
+    got, _ = gather(c3gpu, shards, hybrid(c3gpu, 500))
+    assert oracle.first_diff(want, got) == -1
