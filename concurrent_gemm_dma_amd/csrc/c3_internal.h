@@ -68,7 +68,7 @@ struct GemmPlan {
     const void* B = nullptr;
     void* C = nullptr;
     int M = 0, N = 0, K = 0;
-    int kind = 0;          // 0 = 256x256 tile kernel, 1 = skinny split-K kernel
+    int kind = 0;          // 0 = 256x256 tile kernel, 1 = skinny split-K kernel, 2 = 128x128 tile
     int mt = 1;            // skinny: 16-row MFMA tiles per workgroup (1, 2 or 4)
     int splits = 1;        // skinny: K splits (1 = write bf16 directly)
     int k_per_split = 0;

@@ -11,7 +11,9 @@
 //   epilogue writes 8-byte runs. B stays K x N in LDS and is read with the LDS transpose load
 //   (ds_read_b64_tr_b16), which hands each lane 4 consecutive k of one column. With fewer tiles
 //   than CUs, K can also be split over a second grid dimension (fp32 partials, summed in split
-//   order by splitk_reduce). Every shape with M > 64 uses this kernel.
+//   order by splitk_reduce). Shapes with M > 64 use this kernel unless the 128 kernel wins.
+// * tile128_dma: the same at 128x128 (4 waves of 64x64), two workgroups per CU, for mid-size
+//   shapes where a 256x256 grid leaves most CUs idle and K is too short for a split to pay.
 // * skinny: all M (<= 64) rows x 256 columns per workgroup, K split across workgroups
 //   (deterministic: fp32 partials per split, summed in split order by a second kernel),
 //   v_mfma_f32_16x16x32_bf16. For M <= 64, where the GEMM streams B once and is bound by HBM
@@ -128,7 +130,7 @@ __device__ __forceinline__ void map_tile(int bid, int nblocks, int tiles_m, int 
 // ------------------------------------------------------------------------------------------------
 // 256 x 256 tile kernel, LDS-direct loads
 // ------------------------------------------------------------------------------------------------
-// Same tile, waves and MFMA layout as above, but operands go global -> LDS directly
+// 4 waves (2x2), each 128x128 = 4x4 v_mfma_f32_32x32x16_bf16. Operands go global -> LDS directly
 // (buffer_load_dwordx4 ... lds: each wave-instruction fills 1 KiB of LDS, lane t's 16 bytes at
 // byte 16*t), so no registers stage them. K step 32, four LDS stages of 32 KiB: the loads of
 // step k+4 are issued as soon as every wave has finished reading step k, i.e. about three and a
@@ -435,6 +437,149 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
 }
 
 // ------------------------------------------------------------------------------------------------
+// 128 x 128 tile kernel, LDS-direct loads, two workgroups per CU
+// ------------------------------------------------------------------------------------------------
+// For shapes with fewer 256x256 tiles than CUs. 4 waves (2x2), each 64x64 = 2x2
+// v_mfma_f32_32x32x16_bf16 (64 accumulators per lane), K step 32, four LDS stages of 16 KiB
+// (A [128][32], B [32][128]); two workgroups share a CU, so one's LDS reads and barriers hide
+// behind the other's MFMAs instead of a hand-interleaved schedule.
+namespace tq {
+constexpr int BM = 128, BN = 128, BK = 32, NT = 256, NSTAGE = 4;
+constexpr int A_STAGE = BM * BK * 2;  // 8 KiB: 128 rows of 64 B
+constexpr int B_STAGE = BK * BN * 2;  // 8 KiB: 32 rows of 256 B
+constexpr int STAGE = A_STAGE + B_STAGE;
+constexpr int GROUP_M = 4;
+}  // namespace tq
+
+__global__ __launch_bounds__(256, 2) void gemm_bf16_tile128_dma(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
+    int M, int N, int K, int tiles_m, int tiles_n) {
+    using namespace tq;
+    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int tm, tn;
+    map_tile<GROUP_M>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // ---- global -> LDS: wave w fills A blocks 2w, 2w+1 (16 rows of 64 B each) and B blocks
+    // 2w, 2w+1 (4 k rows of 256 B each); lane t lands at byte 16*t of the 1 KiB block.
+    const i32x4_t rA = make_rsrc_words(A + (size_t)m0 * K, (int64_t)(M - m0) * K * 2);
+    const int a_row0 = 16 * (wave * 2) + (lane >> 2);           // + 16*j
+    const int a_kc = (lane & 3) ^ swz_a32(a_row0);               // same for j = 0, 1
+    const uint32_t a_g0 = (uint32_t)a_row0 * (uint32_t)K * 2u + (uint32_t)a_kc * 16u;
+    const uint32_t a_gstep = 16u * (uint32_t)K * 2u;
+    uint32_t b_g[2];
+    bool b_ok[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int krow = 4 * (wave * 2 + j) + (lane >> 4);
+        const int nc = (lane & 15) ^ swz_b(krow);
+        b_g[j] = (uint32_t)krow * (uint32_t)N * 2u + (uint32_t)nc * 16u;
+        b_ok[j] = (n0 + nc * 8) < N;
+    }
+    auto issue_stage = [&](int k0, int s) {
+        char* As = smem + s * STAGE;
+        char* Bs = As + A_STAGE;
+        const bool a_ok = (k0 + a_kc * 8) < K;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            lds_dma16(rA, As + (wave * 2 + j) * 1024,
+                      a_ok ? a_g0 + (uint32_t)j * a_gstep + (uint32_t)k0 * 2u : kOOB);
+        const i32x4_t rB =
+            make_rsrc_words(B + (size_t)k0 * N + n0, ((int64_t)(K - k0) * N - n0) * 2);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) lds_dma16(rB, Bs + (wave * 2 + j) * 1024, b_ok[j] ? b_g[j] : kOOB);
+    };
+
+    // ---- LDS -> MFMA operands (as in the 256 kernel, with 64-row / 64-column wave tiles) ----
+    const int ar = lane & 31;
+    uint32_t a_rd[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+        a_rd[kk] = (uint32_t)(wm * 64 + ar) * 64u +
+                   (uint32_t)((((kk * 2) + (lane >> 5)) ^ swz_a32(ar)) << 4);
+    const int G = lane >> 4, p = lane & 15;
+    const int b_sw = swz_b(p >> 2);
+    uint32_t b_rd[2];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni) {
+        const int nc = wn * 8 + ni * 4 + 2 * (G & 1) + ((p >> 1) & 1);
+        b_rd[ni] = (uint32_t)(8 * (G >> 1) + (p >> 2)) * 256u + (uint32_t)((nc ^ b_sw) << 4) +
+                   (uint32_t)((p & 1) * 8);
+    }
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = f32x16_t{};
+
+    const int nk = (K + BK - 1) / BK;
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s)
+        if (s < nk) issue_stage(s * BK, s);
+    // stage 0 landed: at most the loads of stages 1 and 2 (4 per stage per wave) outstanding
+    if (nk >= 3) C3_WAIT_VMCNT(8);
+    else if (nk == 2) C3_WAIT_VMCNT(4);
+    else C3_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        // refill the buffer step kt-1 used (every wave finished it before the last barrier)
+        if (kt + NSTAGE - 1 < nk) issue_stage((kt + NSTAGE - 1) * BK, (kt + NSTAGE - 1) & (NSTAGE - 1));
+        const char* As = smem + (kt & (NSTAGE - 1)) * STAGE;
+        const char* Bs = As + A_STAGE;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            bf16x8_t colop[2], rowop[2];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) colop[mi] = lds_load16(As, a_rd[kk] + mi * 2048u);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                rowop[ni] = lds_load_tr8(Bs, b_rd[ni] + kk * 4096u, b_rd[ni] + kk * 4096u + 1024u);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowop[ni], colop[mi],
+                                                                          acc[mi][ni], 0, 0, 0);
+        }
+        // step kt+1 landed for this wave (stages kt+2, kt+3 may be in flight); this wave's
+        // reads of step kt are done; then every wave is past both points
+        const int g = min(max(nk - kt - 2, 0), NSTAGE - 2);
+        if (g >= 2) C3_WAIT_VMCNT(8);
+        else if (g == 1) C3_WAIT_VMCNT(4);
+        else C3_WAIT_VMCNT(0);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+    }
+
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(C + (size_t)m0 * N + n0, ((int64_t)(M - m0) * N - n0) * 2);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+        const int ml = wm * 64 + mi * 32 + (lane & 31);
+        const bool mvalid = (m0 + ml) < M;
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nl = wn * 64 + ni * 32 + 8 * g + 4 * (lane >> 5);
+                const bool ok = mvalid && (n0 + nl) < N;
+                const uint32_t off = ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 2u : kOOB;
+                const f32x16_t& a = acc[mi][ni];
+                store8(rC, off, pack_bf16x4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]));
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------
 // Skinny (small M) split-K kernel
 // ------------------------------------------------------------------------------------------------
 namespace sk {
@@ -656,7 +801,8 @@ int env_int(const char* name, int dflt) {
 // written and read back at about 3.5 TB/s and the reduction launch adds about 4 us. Time of s
 // splits = waves * steps per split * 0.85 (+ partial traffic + 4 if s > 1); the smallest wins,
 // ties to fewer splits. With at least as many tiles as CUs this is always 1.
-int choose_splits(int64_t M, int64_t N, int64_t K, int tiles, int n_cu, int max_splits) {
+int choose_splits(int64_t M, int64_t N, int64_t K, int tiles, int n_cu, int max_splits,
+                  double* t_out) {
     constexpr double kStepUs = 0.85, kPartialBytesPerUs = 3.5e6, kReduceLaunchUs = 4.0;
     int best = 1;
     double best_t = 0.0;
@@ -673,7 +819,17 @@ int choose_splits(int64_t M, int64_t N, int64_t K, int tiles, int n_cu, int max_
             best_t = t;
         }
     }
+    if (t_out) *t_out = best_t;
     return best;
+}
+
+// Time of the 128x128 tile kernel in the same units: two workgroups per CU, about 0.6 us per
+// 32-deep K step of a workgroup (measured on MI355X for 64-576 tiles of 128x128).
+double tile128_time(int64_t M, int64_t N, int64_t K, int n_cu) {
+    constexpr double kStepUs = 0.6;
+    const int64_t tiles = ((M + tq::BM - 1) / tq::BM) * ((N + tq::BN - 1) / tq::BN);
+    const int64_t waves = (tiles + 2 * n_cu - 1) / (2 * n_cu);
+    return (double)waves * (double)((K + tq::BK - 1) / tq::BK) * kStepUs;
 }
 
 }  // namespace
@@ -749,8 +905,20 @@ c3_status gemm_plan(const void* A, const void* B, void* C, int64_t M, int64_t N,
         const int n_cu = ctx().info.n_cu > 0 ? ctx().info.n_cu : 256;
         const int max_splits = std::max(1, std::min(256, (int)(K / (4 * td::BK))));
         int splits = env_int("C3_GEMM_SPLITS", 0);
-        if (splits <= 0) splits = choose_splits(M, N, K, tiles, n_cu, max_splits);
+        double t256 = 0.0;
+        const int auto_splits = choose_splits(M, N, K, tiles, n_cu, max_splits, &t256);
+        if (splits <= 0) splits = auto_splits;
         splits = std::max(1, std::min(splits, max_splits));
+        // With fewer 256x256 tiles than CUs the 128x128 kernel may be faster (more workgroups,
+        // no partial sums); the same model decides. C3_GEMM_TILE=128 / 256 forces the choice.
+        const int tile = env_int("C3_GEMM_TILE", 0);
+        if (tile == 128 ||
+            (tile != 256 && tiles < n_cu && env_int("C3_GEMM_SPLITS", 0) <= 0 &&
+             tile128_time(M, N, K, n_cu) < t256)) {
+            p.kind = 2;
+            *plan = p;
+            return C3_OK;
+        }
         int kps = (int)((K + splits - 1) / splits);
         kps = (kps + td::BK - 1) / td::BK * td::BK;
         splits = (int)((K + kps - 1) / kps);
@@ -778,6 +946,14 @@ c3_status gemm_enqueue(const GemmPlan& p, hipStream_t stream) {
     const auto* A = static_cast<const uint16_t*>(p.A);
     const auto* B = static_cast<const uint16_t*>(p.B);
     auto* C = static_cast<uint16_t*>(p.C);
+    if (p.kind == 2) {
+        const int tiles_m = (p.M + tq::BM - 1) / tq::BM;
+        const int tiles_n = (p.N + tq::BN - 1) / tq::BN;
+        hipLaunchKernelGGL(gemm_bf16_tile128_dma, dim3(tiles_m * tiles_n), dim3(tq::NT), 0, stream,
+                           A, B, C, p.M, p.N, p.K, tiles_m, tiles_n);
+        C3_HIP_TRY(hipGetLastError());
+        return C3_OK;
+    }
     if (p.kind == 0) {
         const int tiles_m = (p.M + td::BM - 1) / td::BM;
         const int tiles_n = (p.N + td::BN - 1) / td::BN;

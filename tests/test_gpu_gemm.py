@@ -98,7 +98,17 @@ def test_gemm_deterministic_and_mask_invariant(c3gpu):
         finally:
             torch.cuda.synchronize()
             c3gpu.c3_stream_destroy(s)
-    # skinny path too
+    # the 128x128 tile kernel (the model's choice for this shape) and the skinny path too
+    A3 = wl.gen_bf16((1000, 1000), ("normal", 0.0, 1.0), 7904)
+    B3 = wl.gen_bf16((1000, 2000), ("normal", 0.0, 0.02), 7905)
+    first3 = run_gemm(c3gpu, A3, B3)
+    mask = c3gpu.c3_cu_mask_balanced(24)
+    s = c3gpu.c3_stream_create(mask)
+    try:
+        np.testing.assert_array_equal(first3, run_gemm(c3gpu, A3, B3, stream=s))
+    finally:
+        torch.cuda.synchronize()
+        c3gpu.c3_stream_destroy(s)
     A2 = wl.gen_bf16((16, 8192), ("normal", 0.0, 1.0), 7902)
     B2 = wl.gen_bf16((8192, 1032), ("normal", 0.0, 0.02), 7903)
     np.testing.assert_array_equal(run_gemm(c3gpu, A2, B2), run_gemm(c3gpu, A2, B2))
@@ -123,6 +133,24 @@ def test_gemm_split_k(c3gpu, M, N, K, monkeypatch):
     monkeypatch.delenv("C3_GEMM_SPLITS")
     Ai = wl.gen_small_int_bf16((M, K), 7960 + K)
     Bi = wl.gen_small_int_bf16((K, N), 7961 + N)
+    np.testing.assert_array_equal(run_gemm(c3gpu, Ai, Bi), oracle.gemm_f32acc(Ai, Bi))
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 128, 32), (300, 264, 72), (1000, 2000, 1000),
+                                   (65, 520, 328), (1024, 776, 1040), (129, 8, 8)])
+def test_gemm_tile128(c3gpu, M, N, K, monkeypatch):
+    """The 128x128 tile kernel (chosen by the cost model for mid-size shapes; forced here with
+    C3_GEMM_TILE=128): oracle tolerance on normal operands, bit-exact on integer-valued ones,
+    same bits on every run."""
+    print(f"tile-128 GEMM {M}x{N}x{K}", flush=True)
+    monkeypatch.setenv("C3_GEMM_TILE", "128")
+    A = wl.gen_bf16((M, K), ("normal", 0.0, 1.0), 7970 + M)
+    B = wl.gen_bf16((K, N), ("normal", 0.0, 0.02), 7971 + N)
+    got = run_gemm(c3gpu, A, B)
+    check_tol(oracle.gemm_f64acc(A, B), got)
+    np.testing.assert_array_equal(got, run_gemm(c3gpu, A, B))
+    Ai = wl.gen_small_int_bf16((M, K), 7980 + K)
+    Bi = wl.gen_small_int_bf16((K, N), 7981 + N)
     np.testing.assert_array_equal(run_gemm(c3gpu, Ai, Bi), oracle.gemm_f32acc(Ai, Bi))
 
 
