@@ -855,6 +855,22 @@ c3_status gemm_validate(const void* A, const void* B, void* C, int64_t M, int64_
     return C3_OK;
 }
 
+// The split-K fp32 workspace of `stream`: grown on demand (hipFree waits for work still using
+// the old one), kept until c3_finalize.
+static c3_status ensure_workspace(hipStream_t stream, size_t need, GemmPlan* p) {
+    Workspace& w = workspaces()[stream];
+    if (w.bytes < need) {
+        if (w.ptr) C3_HIP_TRY(hipFree(w.ptr));
+        w.ptr = nullptr;
+        w.bytes = 0;
+        C3_HIP_TRY(hipMalloc(&w.ptr, need));
+        w.bytes = need;
+    }
+    p->workspace = w.ptr;
+    p->workspace_bytes = need;
+    return C3_OK;
+}
+
 c3_status gemm_plan(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                     hipStream_t stream, GemmPlan* plan) {
     C3_TRY(gemm_validate(A, B, C, M, N, K));
@@ -884,16 +900,7 @@ c3_status gemm_plan(const void* A, const void* B, void* C, int64_t M, int64_t N,
         if (splits > 1) {
             const size_t mpad = (size_t)sk::BM * p.mt;
             const size_t need = (size_t)splits * mpad * (size_t)N * sizeof(float);
-            Workspace& w = workspaces()[stream];
-            if (w.bytes < need) {
-                if (w.ptr) C3_HIP_TRY(hipFree(w.ptr));
-                w.ptr = nullptr;
-                w.bytes = 0;
-                C3_HIP_TRY(hipMalloc(&w.ptr, need));
-                w.bytes = need;
-            }
-            p.workspace = w.ptr;
-            p.workspace_bytes = need;
+            C3_TRY(ensure_workspace(stream, need, &p));
         }
     } else {
         p.kind = 0;
@@ -926,16 +933,7 @@ c3_status gemm_plan(const void* A, const void* B, void* C, int64_t M, int64_t N,
         p.k_per_split = splits > 1 ? kps : (int)K;
         if (splits > 1) {
             const size_t need = (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
-            Workspace& w = workspaces()[stream];
-            if (w.bytes < need) {
-                if (w.ptr) C3_HIP_TRY(hipFree(w.ptr));
-                w.ptr = nullptr;
-                w.bytes = 0;
-                C3_HIP_TRY(hipMalloc(&w.ptr, need));
-                w.bytes = need;
-            }
-            p.workspace = w.ptr;
-            p.workspace_bytes = need;
+            C3_TRY(ensure_workspace(stream, need, &p));
         }
     }
     *plan = p;
