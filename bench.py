@@ -4,9 +4,9 @@ copy, moved by the SDMA engines (headline) and by a CU kernel (baseline).
 
 Default mode (`--mode c3`, the contract): a step is one concurrent run (c3_run_concurrent) of
 the whole path over the workload: GEMM and copy issued (communication first), both completed.
-Every round runs the isolated GEMM and, per mover, the isolated copy then the concurrent step;
-the order of these units rotates from round to round, so clock and thermal drift hit isolated
-and concurrent times, and every mover, alike. Before
+Every round runs the isolated GEMM and, per mover, the isolated copy then the concurrent step,
+in an order shuffled per round (fixed seeds), so clock and thermal drift hit isolated and
+concurrent times, and every mover, alike. Before
 every run, untimed: outputs poisoned, then the library reads 512 MiB of scratch (Infinity Cache
 flush) before its clock starts. After every run, untimed: each destination range is compared
 byte for byte with its source on the device (the copy's definition) and C bit for bit with the
@@ -43,6 +43,7 @@ import argparse
 import hashlib
 import json
 import os
+import random
 import statistics
 import sys
 import time
@@ -351,17 +352,18 @@ def run_c3(args, c3, info):
     state_before = gpu_state()
     wall0 = time.time()
     # One round runs the isolated GEMM and, per mover, its isolated copy then its concurrent
-    # step. The order of these units rotates from round to round, so that every unit takes every
-    # position equally often and the clock drift within a round (a long GEMM heats the chip)
-    # biases no cell.
+    # step, in an order shuffled per round (seeded by the round number), so that no cell always
+    # takes the same position or follows the same neighbour: the state a long GEMM leaves the
+    # chip in (clock, temperature) then biases no cell.
     units = ["gemm"] + [name for name, _ in movers]
     for i in range(args.warmup + args.steps):
         if i == args.warmup:
             torch.cuda.synchronize()
             wall0 = time.time()
         timed = i >= args.warmup
-        k = i % len(units)
-        for name in units[k:] + units[:k]:
+        order = list(units)
+        random.Random(1000 + i).shuffle(order)
+        for name in order:
             if name == "gemm":
                 s.poison()
                 t = c3.c3_run_concurrent(s.gargs, None, iso_g_opts)
@@ -571,10 +573,12 @@ def run_grid(args, c3, info):
             s.poison()
             rnd["gemm"] = c3.c3_run_concurrent(s.gargs, None, c3.conc_opts(flush_bytes=FLUSH_BYTES))["t_conc_ns"]
             s.verify_c("grid isolated GEMM")
-            # movers in rotating order (round 0 in list order: the hybrid's share needs the
-            # other two movers' isolated times first)
-            k = i % len(names)
-            for mname in names[k:] + names[:k]:
+            # movers in an order shuffled per round (round 0 in list order: the hybrid's share
+            # needs the other two movers' isolated times first)
+            order = list(names)
+            if i:
+                random.Random(2000 + i).shuffle(order)
+            for mname in order:
                 if mname == "hybrid":
                     if pm < 0:  # chosen once, from the untimed first round's isolated times
                         pm = c3.c3_hybrid_share(rnd["gemm"] * 1e-9, rnd[("copy", "sdma")] * 1e-9,
@@ -901,8 +905,8 @@ def run_hybrid(args, c3, info):
                     hyb[chosen] = s.cargs(c3.C3_MOVER_HYBRID, c3.move_opts(sdma_permille=chosen))
                     conc[chosen] = []
             order = sorted(hyb)
-            k = i % len(order)  # rotating order: no share always runs last in a round
-            for pm in order[k:] + order[:k]:
+            random.Random(3000 + i).shuffle(order)  # no share always runs in the same place
+            for pm in order:
                 s.poison()
                 t = c3.c3_run_concurrent(s.gargs, hyb[pm][0], conc_opts)
                 s.verify_copy(f"hybrid {pm}")
