@@ -5,7 +5,7 @@
 // of an 8x8 all-to-all. Also: a last-level-cache flush and a CU placement probe.
 //
 // Vector path: every lane moves 16-byte pieces; a workgroup owns a contiguous run of pieces
-// across the concatenated segments, issues all of its loads before its stores (UNROLL pieces per
+// across the concatenated segments, issues all of its loads before its stores (kUnroll pieces per
 // lane in flight), and a wavefront covers 1 KiB of contiguous bytes per access. Pieces that are
 // not 16-byte aligned on both sides, and segment tails shorter than 16 bytes, go to a byte path.
 #include "c3_internal.h"
