@@ -171,3 +171,21 @@ def test_hybrid_share_closed_forms(c3):
         with pytest.raises(c3.C3Error):
             c3.c3_hybrid_share(*bad)
 
+
+def test_readme_c_example_compiles(tmp_path):
+    """The C usage example in README.md compiles against include/c3.h as C11."""
+    import re
+    import shutil
+    import subprocess
+
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    readme = open(os.path.join(os.path.dirname(HEADER), "..", "README.md")).read()
+    blocks = re.findall(r"```c\n(.*?)```", readme, re.S)
+    assert blocks, "README.md has no C example"
+    src = tmp_path / "example.c"
+    src.write_text(blocks[0])
+    r = subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-fsyntax-only", "-I",
+                        os.path.dirname(HEADER), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
