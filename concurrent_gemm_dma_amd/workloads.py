@@ -150,6 +150,21 @@ def gen_bytes(nbytes: int, seed: int) -> np.ndarray:
     return rng.integers(0, 256, size=nbytes, dtype=np.uint8)
 
 
+def gen_tagged_shards(n_shards: int, shard_bytes: int) -> list:
+    """Gather sources in the diagnostic pattern: every little-endian 8-byte word of shard i holds
+    (i << 56) | d, d = the byte offset where that word belongs in the gathered buffer
+    (i * shard_bytes + its offset in the shard). A word found anywhere else names its shard and
+    its place. shard_bytes must be a multiple of 8; n_shards at most 256."""
+    if shard_bytes % 8 or not 0 <= n_shards <= 256:
+        raise ValueError("tagged shards need shard_bytes % 8 == 0 and 0 <= n_shards <= 256")
+    words = shard_bytes // 8
+    out = []
+    for i in range(n_shards):
+        d = np.arange(words, dtype=np.uint64) * np.uint64(8) + np.uint64(i * shard_bytes)
+        out.append((d | (np.uint64(i) << np.uint64(56))).astype("<u8").view(np.uint8))
+    return out
+
+
 def gen_gemm_operands(w: Workload, int_exact: bool = False):
     """(A [M,K], B [K,N]) as uint16 bf16 bit patterns."""
     if int_exact:

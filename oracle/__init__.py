@@ -308,6 +308,30 @@ def first_diff(a: np.ndarray, b: np.ndarray) -> int:
     return int(lib().orc_first_diff(va.ctypes.data, vb.ctypes.data, va.size))
 
 
+def explain_tagged_gather(got: np.ndarray, n_shards: int, shard_bytes: int,
+                          limit: int = 16) -> list:
+    """For a gather of shards in the tagged pattern (each 8-byte word = shard << 56 | the byte
+    offset where it belongs): the misplaced words of `got`, as (offset in got, shard found,
+    offset the found word belongs at), at most `limit` of them; [] when every word is in place.
+    Offset -1 / shard -1 mark a word that carries no valid tag (never written, or torn)."""
+    g = np.ascontiguousarray(got).view(np.uint8).reshape(-1)
+    if shard_bytes % 8 or g.size != n_shards * shard_bytes:
+        raise ValueError("explain_tagged_gather: size must be n_shards * shard_bytes, "
+                         "shard_bytes a multiple of 8")
+    words = g.view("<u8")
+    want = np.arange(words.size, dtype=np.uint64) * np.uint64(8)
+    want |= (want // np.uint64(max(shard_bytes, 1))) << np.uint64(56)
+    bad = np.flatnonzero(words != want)[:limit]
+    out = []
+    for w in bad:
+        v = int(words[w])
+        shard, off = v >> 56, v & ((1 << 56) - 1)
+        valid = (shard < n_shards and off % 8 == 0 and off < g.size
+                 and off // shard_bytes == shard)
+        out.append((int(w) * 8, shard if valid else -1, off if valid else -1))
+    return out
+
+
 def gemm_compare(ref: np.ndarray, got: np.ndarray, tol: float = 1e-2) -> dict:
     r = np.ascontiguousarray(ref, dtype=np.uint16).reshape(-1)
     g = np.ascontiguousarray(got, dtype=np.uint16).reshape(-1)

@@ -12,6 +12,7 @@ from concurrent_gemm_dma_amd import workloads as wl
 from gpu_util import bf16_from_dev, bytes_from_dev, empty_bf16, empty_bytes, to_dev
 
 pytestmark = pytest.mark.gpu
+KiB = 1 << 10
 MiB = 1 << 20
 
 
@@ -230,6 +231,30 @@ def test_concurrent_allreduce_isolated_and_skinny(c3gpu):
         t = c3gpu.c3_run_concurrent(None, cargs, c3gpu.conc_opts(flush_bytes=64 * MiB))
         case.check_comm(f"isolated all-reduce, mover {mover}")
         assert t["t_gemm_done_ns"] == 0 and t["t_copy_done_ns"] > 0 and t["reduce_gpu_ms"] > 0
+
+
+def test_concurrent_tagged_gather(c3gpu):
+    """A gather in the diagnostic pattern (each 8-byte word = shard << 56 | its destination
+    offset) overlapped with a GEMM, for every mover: any word out of place is named."""
+    c3 = c3gpu
+    n, sb = 8, MiB
+    case = Case(c3, 1000, 2000, 1000, "gather", n, sb, 7100)
+    case.src_np = wl.gen_tagged_shards(n, sb)
+    case.src = [to_dev(s) for s in case.src_np]
+    case.want = oracle.gather(case.src_np)
+    cells = [(c3.C3_MOVER_CU, None), (c3.C3_MOVER_SDMA, c3.move_opts(chunk_bytes=96 * KiB)),
+             (c3.C3_MOVER_HYBRID, c3.move_opts(sdma_permille=400))]
+    for r, (m, opts) in enumerate(cells, start=1):
+        for comm_first in (False, True):
+            case.poison(2 * r + comm_first)
+            cargs, _keep = case.cargs(c3, m, opts)
+            c3.c3_run_concurrent(case.gargs(c3), cargs, c3.conc_opts(comm_first=comm_first))
+            label = f"tagged gather mover={m} comm_first={comm_first}"
+            print(label, flush=True)
+            assert oracle.explain_tagged_gather(bytes_from_dev(case.dst), n, sb) == [], label
+            case.check_comm(label)
+            rep = oracle.gemm_compare(case.ref, bf16_from_dev(case.dC))
+            assert oracle.gemm_within_tolerance(rep), (label, rep)
 
 
 def test_isolated_copy_via_run_concurrent(c3gpu):

@@ -17,7 +17,7 @@ MiB = 1 << 20
 
 
 def mover_id(c3, name):
-    return c3.C3_MOVER_CU if name == "cu" else c3.C3_MOVER_SDMA
+    return {"cu": c3.C3_MOVER_CU, "sdma": c3.C3_MOVER_SDMA, "hybrid": c3.C3_MOVER_HYBRID}[name]
 
 
 def sync():
@@ -47,6 +47,21 @@ def test_gather(c3gpu, mover, n, sb):
     got, whole = do_gather(c3gpu, shards, mover)
     assert oracle.first_diff(oracle.gather(shards), got) == -1
     assert whole[-1] == 0xA5  # nothing written past the end
+
+
+@pytest.mark.parametrize("mover,kw", [("cu", {}), ("sdma", {}), ("sdma", {"chunk_bytes": 40 * KiB}),
+                                       ("hybrid", {"sdma_permille": 500}),
+                                       ("hybrid", {"sdma_permille": 137, "chunk_bytes": 64 * KiB})])
+@pytest.mark.parametrize("n,sb", [(8, 2 * MiB + 8), (5, 24 * KiB)])
+def test_gather_tagged(c3gpu, mover, kw, n, sb):
+    """The diagnostic pattern: each 8-byte word carries its shard and its destination offset, so
+    a misplaced, swapped or missing word is reported by name."""
+    print(f"tagged gather mover={mover} opts={kw} n={n} shard={sb}", flush=True)
+    shards = wl.gen_tagged_shards(n, sb)
+    got, whole = do_gather(c3gpu, shards, mover, c3gpu.move_opts(**kw) if kw else None)
+    assert oracle.explain_tagged_gather(got, n, sb) == []
+    assert oracle.first_diff(oracle.gather(shards), got) == -1
+    assert whole[-1] == 0xA5
 
 
 @pytest.mark.parametrize("mover", MOVERS)

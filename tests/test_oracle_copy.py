@@ -93,3 +93,37 @@ def test_gemm_compare_flags(orc):
     rep = orc.gemm_compare(ref, one_ulp)
     assert rep["n_violations"] == 0
     assert rep["frob_rel"] > 1e-3  # ~half the elements off by one ulp is too much in aggregate
+
+
+def test_tagged_pattern_and_attribution(orc):
+    """The diagnostic gather pattern: every 8-byte word names its shard and the place it belongs,
+    so a misplaced, swapped or missing word is attributed. The checker is pinned on planted
+    mistakes in the oracle's own gather."""
+    n, sb = 8, 4096
+    shards = wl.gen_tagged_shards(n, sb)
+    good = orc.gather(shards)
+    assert orc.explain_tagged_gather(good, n, sb) == []
+    # word 5 of shard 2 as a plain number: shard 2 in the top byte, destination 2*4096 + 40
+    assert int(shards[2][40:48].view("<u8")[0]) == (2 << 56) | (2 * sb + 40)
+
+    swapped = good.copy()
+    a, b = 2 * sb + 64, 5 * sb + 8                      # two words exchanged across shards
+    swapped[a:a + 8], swapped[b:b + 8] = good[b:b + 8].copy(), good[a:a + 8].copy()
+    assert orc.explain_tagged_gather(swapped, n, sb) == [(a, 5, b), (b, 2, a)]
+
+    dropped = good.copy()
+    dropped[3 * sb + 16:3 * sb + 24] = 0xA5             # never written: poison remains
+    assert orc.explain_tagged_gather(dropped, n, sb) == [(3 * sb + 16, -1, -1)]
+
+    shifted = good.copy()
+    shifted[4 * sb:5 * sb] = good[3 * sb:4 * sb]        # shard 3 landed in shard 4's slot
+    rep = orc.explain_tagged_gather(shifted, n, sb, limit=4)
+    assert rep == [(4 * sb + 8 * w, 3, 3 * sb + 8 * w) for w in range(4)]
+
+    torn = good.copy()
+    torn[6 * sb + 3] ^= 0x10                            # one byte flipped inside a word
+    assert orc.explain_tagged_gather(torn, n, sb) == [(6 * sb, -1, -1)]  # no valid tag left
+    with pytest.raises(ValueError):
+        orc.explain_tagged_gather(good[:-8], n, sb)
+    with pytest.raises(ValueError):
+        wl.gen_tagged_shards(2, 12)
