@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 from concurrent_gemm_dma_amd import workloads as wl
+from epilogue_cases import epilogue_case
 from gpu_util import bf16_from_dev, empty_bf16, to_dev
 
 pytestmark = pytest.mark.gpu
@@ -80,6 +81,47 @@ def test_gemm_zero(c3gpu):
     B = wl.gen_bf16((136, 264), ("normal", 0.0, 1.0), 7800)
     got = run_gemm(c3gpu, A, B)
     assert np.all(oracle.bf16_to_f32(got) == 0.0)
+
+
+@pytest.mark.parametrize("rows,ts", [
+    # every sign and mantissa at the lowest covered, the unit and the highest exponent (where
+    # the largest mantissas round up to infinity)
+    ("all", (-103, -1, 0, 1, 64, 126, 127, 100)),
+    # a mantissa sample (every rounding case: round bits 0x0000-0xFFFF below 7 kept bits) at every
+    # covered exponent
+    ("sample", tuple(range(-103, 128)) + (0,)),
+    # the skinny kernel's epilogue (M <= 64)
+    ("skinny", tuple(range(-103, 128)) + (0,)),
+])
+def test_gemm_epilogue_rounding_sweep(c3gpu, rows, ts):
+    """The epilogue's fp32 -> bf16 conversion over every fp32 pattern with exponent field
+    24..254 (all 2^24 sign x mantissa patterns at eight exponents, a 2^16 sample at all 231),
+    bit-exact against the oracle's nearest-even converter. Exponents below 24, subnormals and
+    non-finite sums are outside what exact bf16 products can build here."""
+    if rows == "all":
+        idx = np.arange(1 << 24, dtype=np.uint32)
+        sign, f = (idx >> 23).astype(bool), idx & 0x7FFFFF
+    elif rows == "sample":
+        # every value of the 16 bits rounding drops, with kept bits and sign varied
+        low = np.arange(1 << 16, dtype=np.uint32)
+        kept = (low * 2654435761 >> 9) & 0x7F
+        f = (kept << 16) | low
+        sign = (low & 1).astype(bool)
+    else:
+        low = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x4000, 0xC000] * 8, np.uint32)
+        kept = np.repeat(np.array([0, 1, 0x7E, 0x7F, 2, 3, 0x40, 0x41], np.uint32), 8)
+        f = (kept << 16) | low
+        sign = (np.arange(64) % 3 == 0)
+    block = 1 << 21                                   # the largest M one call takes
+    for r0 in range(0, f.size, block):
+        A, B, pattern = epilogue_case(sign[r0:r0 + block], f[r0:r0 + block], list(ts))
+        print(f"epilogue sweep {rows}: rows {r0}.. M={A.shape[0]} N={B.shape[1]} K=8", flush=True)
+        got = run_gemm(c3gpu, A, B).reshape(-1)
+        want = oracle.bf16_from_f32_bits(pattern.reshape(-1))
+        pattern = pattern.reshape(-1)
+        bad = np.flatnonzero(got != want)
+        assert bad.size == 0, (f"{bad.size} mismatches, first at pattern {int(pattern[bad[0]]):#010x}: "
+                               f"got {int(got[bad[0]]):#06x}, want {int(want[bad[0]]):#06x}")
 
 
 def test_gemm_deterministic_and_mask_invariant(c3gpu):

@@ -4,7 +4,7 @@ bound, exact integer arithmetic, and identity / zero invariants."""
 import numpy as np
 import pytest
 
-from bf16_ref import bf16_rne_reference_f64
+from bf16_ref import bf16_rne_reference_f32_bits, bf16_rne_reference_f64
 from concurrent_gemm_dma_amd import workloads as wl
 
 U = 2.0 ** -24  # unit roundoff of fp32
@@ -139,3 +139,21 @@ def test_fp32_and_fp64_references_close(orc):
     B = _rand_bf16((512, 48), 1401, 0.02)
     rep = orc.gemm_compare(orc.gemm_f64acc(A, B), orc.gemm_f32acc(A, B), 1e-2)
     assert rep["n_violations"] == 0 and rep["frob_rel"] < 1e-3
+
+
+def test_epilogue_sweep_construction_is_exact(orc):
+    """The epilogue sweep's operands: the exact (fp64) sum of every row and column equals the
+    intended fp32 pattern, so the oracle's fp32-accumulate GEMM must round it exactly as the
+    independent nearest-even formulation rounds the pattern."""
+    from epilogue_cases import epilogue_case
+
+    rng = np.random.Generator(np.random.PCG64(0xE9))
+    idx = rng.integers(0, 1 << 24, size=2000).astype(np.uint32)
+    sign, f = (idx >> 23).astype(bool), idx & 0x7FFFFF
+    ts = list(range(-103, 128)) + [0]
+    A, B, pattern = epilogue_case(sign, f, ts)
+    exact = orc.bf16_to_f32(A).astype(np.float64) @ orc.bf16_to_f32(B).astype(np.float64)
+    np.testing.assert_array_equal(exact, pattern.view(np.float32).astype(np.float64))
+    want = bf16_rne_reference_f32_bits(pattern.reshape(-1)).reshape(pattern.shape)
+    np.testing.assert_array_equal(orc.gemm_f32acc(A, B), want)
+    assert np.any((want & 0x7FFF) == 0x7F80)        # the top exponent's round-ups overflow
