@@ -448,7 +448,13 @@ def run_c3(args, c3, info):
                if w.copy == "allreduce" else {}),
             **{k: m[k] for k in ("ideal_speedup", "speedup", "uplift_fraction", "ratio_of_ideal",
                                  "gemm_slowdown", "hbm_ceiling", "taxonomy")},
+            # overlap cannot beat running both at their isolated speeds: a realized speedup above
+            # the ideal means the isolated times were measured slow (a measurement anomaly)
+            "anomaly_speedup_above_ideal": bool(m["speedup"] > m["ideal_speedup"] * 1.001),
         }
+        if results[name]["anomaly_speedup_above_ideal"]:
+            log(f"{name}: WARNING realized speedup {m['speedup']:.4f} above the ideal "
+                f"{m['ideal_speedup']:.4f}: isolated timings suspect")
         log(f"{name}: T_copy {T_copy * 1e3:.3f} ms ({results[name]['copy_gbps_isolated']:.0f} GB/s), "
             f"T_conc {T_conc * 1e3:.3f} ms, S {m['speedup']:.4f} / ideal {m['ideal_speedup']:.4f}, "
             f"uplift {m['uplift_fraction'] * 100:.1f}%")

@@ -46,8 +46,10 @@ def test_gemm_random_normal(c3gpu, M, N, K):
     A = wl.gen_bf16((M, K), ("normal", 0.0, 1.0), 7000 + M)
     B = wl.gen_bf16((K, N), ("normal", 0.0, 0.02), 7100 + N + K)
     got = run_gemm(c3gpu, A, B)
-    check_tol(oracle.gemm_f64acc(A, B), got)
+    rep = check_tol(oracle.gemm_f64acc(A, B), got)
     check_tol(oracle.gemm_f32acc(A, B), got)
+    # bf16 against bf16: only sums that straddle a rounding boundary may differ, far under 1%
+    assert rep["n_diff"] <= max(2, rep["n"] // 100), rep
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 512, 512), (17, 520, 328), (600, 520, 328)])
