@@ -6,7 +6,8 @@
 //
 // * tile256_dma: 256x256 output tile per workgroup, 4 waves (2x2), each wave 128x128 built from
 //   4x4 v_mfma_f32_32x32x16_bf16. Operands go global -> LDS directly (LDS-direct buffer loads),
-//   K step 32, four LDS stages. The MFMA is fed transposed (B^T as the row operand, A^T as the
+//   K step 32: A in slabs of 64 k (full 128-byte lines), three in LDS, B in four 32-k stages.
+//   The MFMA is fed transposed (B^T as the row operand, A^T as the
 //   column operand), so each lane's accumulators are 4 consecutive columns of one C row and the
 //   epilogue writes 8-byte runs. B stays K x N in LDS and is read with the LDS transpose load
 //   (ds_read_b64_tr_b16), which hands each lane 4 consecutive k of one column. With fewer tiles
@@ -132,18 +133,18 @@ __device__ __forceinline__ void map_tile(int bid, int nblocks, int tiles_m, int 
 // ------------------------------------------------------------------------------------------------
 // 4 waves (2x2), each 128x128 = 4x4 v_mfma_f32_32x32x16_bf16. Operands go global -> LDS directly
 // (buffer_load_dwordx4 ... lds: each wave-instruction fills 1 KiB of LDS, lane t's 16 bytes at
-// byte 16*t), so no registers stage them. K step 32, four LDS stages of 32 KiB: the loads of
-// step k+4 are issued as soon as every wave has finished reading step k, i.e. about three and a
-// half steps of MFMA work before they are needed. Per step: read the second half of this step's
-// fragments, run the first half's MFMAs, wait for step k+1 and barrier, refill this step's
-// buffer, read the first half of step k+1's fragments, run the second half's MFMAs.
+// byte 16*t), so no registers stage them. K step 32. A is loaded in slabs of 64 k (each row's
+// 128 bytes whole, so every L1 -> L2 request is a full line: a third fewer requests than 64-byte
+// half rows, and less power under the chip's power limit), three slabs in LDS (96 KiB), each
+// serving two steps; B in four stages of 32 k (64 KiB). Each step issues B of step k+3 and one
+// half (128 rows) of the slab four to five steps ahead. Per step: read the second half of this
+// step's fragments, run the first half's MFMAs, wait for step k+1 and barrier, issue the A half,
+// read the first half of step k+1's fragments, run the second half's MFMAs.
 namespace td {
-constexpr int BM = 256, BN = 256, BK = 32, NT = 256, NSTAGE = 4;
-constexpr int A_STAGE = BM * BK * 2;  // 16 KiB: 256 rows of 64 B
+constexpr int BM = 256, BN = 256, BK = 32, NT = 256, NSTAGE = 4;  // NSTAGE: B stages
 constexpr int B_STAGE = BK * BN * 2;  // 16 KiB: 32 rows of 512 B
-constexpr int STAGE = A_STAGE + B_STAGE;
 constexpr int GROUP_M = 4;            // tile rows walked together on one XCD (map_tile)
-constexpr int LOADS_PER_STAGE = 8;    // per wave: 4 A + 4 B wave-instructions
+constexpr int LOADS_PER_STAGE = 8;    // per wave and step: 4 A (half slab) + 4 B wave-instructions
 }  // namespace td
 
 // A rows of 64 B (4 chunks): chunk ^= 2*(r2^r3) + (r1^r2) (r_i = bit i of the row). Distinct
@@ -188,6 +189,18 @@ __device__ __forceinline__ void lds_dma16_at(i32x4_t r, uint32_t lds_addr, uint3
         : "memory", "m0");
 }
 
+template <uint32_t OFF>
+__device__ __forceinline__ void lds_dma16_so(i32x4_t r, uint32_t lds_base, uint32_t voff,
+                                             uint32_t soff) {
+    asm volatile(
+        "s_add_u32 m0, %0, %4\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(lds_base), "v"(voff), "s"(r), "s"(soff), "n"(OFF)
+        : "memory", "m0", "scc");
+}
+
 __device__ __forceinline__ void lds_dma16(i32x4_t r, char* lds, uint32_t voff) {
     lds_dma16_at(r, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(C3_LDS char*)lds), voff);
 }
@@ -200,7 +213,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, uint16_t* __restrict__ C,
     float* __restrict__ ws, int M, int N, int K, int k_per_split, int tiles_m, int tiles_n) {
     using namespace td;
-    __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * STAGE];
+    // A in slabs of 64 k ([256 rows][128 B], three buffers); B in 32-k stages (four buffers)
+    constexpr int A_SLAB = BM * 64 * 2;                     // 32 KiB
+    constexpr int B_REGION = 3 * A_SLAB;                    // 96 KiB
+    __shared__ __attribute__((aligned(1024))) char smem[B_REGION + NSTAGE * B_STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -218,14 +234,22 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         B += (size_t)kbeg * N;
     }
 
-    // ---- global -> LDS addressing. Wave w fills A blocks w*4+j (16 rows each) and B blocks
-    // w*4+j (2 k rows each), j = 0..3; lane t lands at byte 16*t of the 1 KiB block.
+    // ---- global -> LDS addressing. Wave w fills, per A half slab, blocks 4w+i (8 rows each)
+    // and, per B stage, blocks 4w+j (2 k rows each); lane t lands at byte 16*t of the 1 KiB
+    // block.
     const i32x4_t rA =
         make_rsrc_words(A + (size_t)m0 * K, (int64_t)(M - m0) * K * 2 - (int64_t)kbeg * 2);
-    const int a_row0 = 16 * (wave * 4) + (lane >> 2);           // + 16*j
-    const int a_kc = (lane & 3) ^ swz_a32(a_row0);               // same for every j
-    const uint32_t a_g0 = (uint32_t)a_row0 * (uint32_t)K * 2u + (uint32_t)a_kc * 16u;
-    const uint32_t a_gstep = 16u * (uint32_t)K * 2u;
+    // half h of slab j: wave w, instruction i covers rows 128h + 32w + 8i + lane/8, 128 B each;
+    // lane t lands at chunk position t%8 and loads global chunk (t%8) ^ swz_a(row)
+    int a_c[4];
+    uint32_t a_g[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = 32 * wave + 8 * i + (lane >> 3);
+        a_c[i] = (lane & 7) ^ swz_a(row);
+        a_g[i] = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)a_c[i] * 16u;
+    }
+    const uint32_t a_hstep = 128u * (uint32_t)K * 2u;
     uint32_t b_g[4];
     bool b_ok[4];
 #pragma unroll
@@ -235,27 +259,30 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         b_g[j] = (uint32_t)krow * (uint32_t)N * 2u + (uint32_t)nc * 16u;
         b_ok[j] = (n0 + nc * 8) < N;
     }
-    auto issue_stage = [&](int k0, int s) {
-        char* As = smem + s * STAGE;
-        char* Bs = As + A_STAGE;
-        const bool a_ok = (k0 + a_kc * 8) < Ke;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            lds_dma16(rA, As + (wave * 4 + j) * 1024,
-                      a_ok ? a_g0 + (uint32_t)j * a_gstep + (uint32_t)k0 * 2u : kOOB);
+    auto issue_B = [&](int k0, int st) {
         const i32x4_t rB =
             make_rsrc_words(B + (size_t)k0 * N + n0, ((int64_t)(Ke - k0) * N - n0) * 2);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) lds_dma16(rB, Bs + (wave * 4 + j) * 1024, b_ok[j] ? b_g[j] : kOOB);
+        for (int j = 0; j < 4; ++j)
+            lds_dma16(rB, smem + B_REGION + st * B_STAGE + (wave * 4 + j) * 1024, b_ok[j] ? b_g[j] : kOOB);
+    };
+    auto issue_A_half = [&](int slab, int h) {
+        const int k0 = 64 * slab;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = (k0 + a_c[i] * 8) < Ke;
+            lds_dma16(rA, smem + (slab % 3) * A_SLAB + (16 * h + 4 * wave + i) * 1024,
+                      ok ? a_g[i] + (uint32_t)h * a_hstep + (uint32_t)k0 * 2u : kOOB);
+        }
     };
 
     // ---- LDS -> MFMA operand addressing ----
     const int ar = lane & 31;
-    uint32_t a_rd[2];
+    uint32_t a_rd[2];  // even step; an odd step reads chunk + 4, i.e. byte offset ^ 64
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
-        a_rd[kk] = (uint32_t)(wm * 128 + ar) * 64u +
-                   (uint32_t)((((kk * 2) + (lane >> 5)) ^ swz_a32(ar)) << 4);
+        a_rd[kk] = (uint32_t)(wm * 128 + ar) * 128u +
+                   (uint32_t)((((kk * 2) + (lane >> 5)) ^ swz_a(ar)) << 4);
     const int G = lane >> 4, p = lane & 15;
     const int b_sw = swz_b(p >> 2);
     uint32_t b_rd[4];
@@ -273,24 +300,18 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x16_t{};
 
     const int nk = (Ke + BK - 1) / BK;
-    // Split refill: a stage's A half is issued one half-step earlier than its B half, so the
-    // prologue issues stages 0..2 whole and only the A half of stage 3.
-#pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s)
-        if (s < nk) issue_stage(s * BK, s);
-    if (nk > NSTAGE - 1) {
-        const int k0 = (NSTAGE - 1) * BK;
-        const bool a_ok = (k0 + a_kc * 8) < Ke;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            lds_dma16(rA, smem + (NSTAGE - 1) * STAGE + (wave * 4 + j) * 1024,
-                      a_ok ? a_g0 + (uint32_t)j * a_gstep + (uint32_t)k0 * 2u : kOOB);
-    }
-    // loads issued after stage 0's last one: A1 B1 A2 B2 A3 (those that exist)
-    if (nk >= 4) C3_WAIT_VMCNT(5 * 4);
-    else if (nk == 3) C3_WAIT_VMCNT(4 * 4);
-    else if (nk == 2) C3_WAIT_VMCNT(2 * 4);
-    else C3_WAIT_VMCNT(0);
+    // Prologue, in the order the steady state issues (step kt issues B of step kt+3, then half
+    // 1 - kt%2 of slab (kt+5)/2): slab 0, B0, slab 1 first half, B1, slab 1 second half, B2,
+    // slab 2 first half. Loads past the end read zeros into buffers nothing reads.
+    issue_A_half(0, 0);
+    issue_A_half(0, 1);
+    issue_B(0, 0);
+    issue_A_half(1, 0);
+    issue_B(BK, 1);
+    issue_A_half(1, 1);
+    issue_B(2 * BK, 2);
+    issue_A_half(2, 0);
+    C3_WAIT_VMCNT(5 * 4);  // slab 0 and B0 landed
     __syncthreads();
 
     // With one wave per SIMD the MFMA pipe idles whenever the wave issues anything else between
@@ -300,11 +321,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     // the moment the pipe frees.
     bf16x8_t cf[2][4];
     i16x4_t rlo[2][4], rhi[2][4];
-    auto read_item = [&](int s, int kk, int set, int j) {
-        const char* As = smem + s * STAGE;
-        const char* Bs = As + A_STAGE;
+    // kt: the step whose fragments are read (A slab kt/2, parity kt%2; B stage kt%4)
+    auto read_item = [&](int kt, int kk, int set, int j) {
+        const char* As = smem + ((kt >> 1) % 3) * A_SLAB;
+        const char* Bs = smem + B_REGION + (kt & (NSTAGE - 1)) * B_STAGE;
         if (j < 4) {
-            cf[set][j] = lds_load16(As, a_rd[kk] + j * 2048u);
+            cf[set][j] = lds_load16(As, (a_rd[kk] ^ ((uint32_t)(kt & 1) << 6)) + j * 4096u);
         } else {
             const int ni = (j - 4) >> 1;
             const uint32_t off = b_rd[ni] + kk * 8192u + ((j - 4) & 1) * 2048u;
@@ -323,14 +345,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     // Wave-uniform LDS byte addresses of this wave's LDS-direct destinations in stage 0.
     const uint32_t lds_base = (uint32_t)(uintptr_t)(C3_LDS char*)smem;
     const uint32_t wave_u = __builtin_amdgcn_readfirstlane((uint32_t)wave);
-    const uint32_t a_dst0 = lds_base + wave_u * 4096u;
-    const uint32_t b_dst0 = lds_base + (uint32_t)A_STAGE + wave_u * 4096u;
+    const uint32_t b_dst0 = lds_base + (uint32_t)B_REGION + wave_u * 4096u;
 
     // One K step, with compile-time flags (each loop body stays straight-line: branches around
     // the MFMA sequence cost the accumulators their registers):
     //   BA - first half issues the B half of step kt+3 into buffer (kt+3)%4 (split refill; that
     //        buffer's last reader, step kt-1, finished before the previous step's barrier),
-    //   RA - second half issues the A half of step kt+4 into this step's buffer,
+    //   RA - second half issues half 1 - kt%2 of slab (kt+5)/2 (rows 128h..128h+127),
     //   NX - second half reads step kt+1's first fragments.
     auto step = [&](int kt, auto ba_c, auto ra_c, auto nx_c) {
         constexpr bool BA = decltype(ba_c)::value;
@@ -341,12 +362,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         const int k3 = (kt + NSTAGE - 1) * BK;
         i32x4_t rB3{};
         if (BA) rB3 = make_rsrc_words(B + (size_t)k3 * N + n0, ((int64_t)(Ke - k3) * N - n0) * 2);
-        const uint32_t b_dst3 = b_dst0 + (uint32_t)s3 * STAGE;
+        const uint32_t b_dst3 = b_dst0 + (uint32_t)s3 * B_STAGE;
         // first half: MFMAs of k-slice 0 (set 0) with the reads of k-slice 1 (set 1)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             mfma_item(0, i);
-            if (i < 12) read_item(s, 1, 1, i);
+            if (i < 12) read_item(kt, 1, 1, i);
             if (BA && i >= 4 && i < 8)
                 lds_dma16_at(rB3, b_dst3 + (i - 4) * 1024u, b_ok[i - 4] ? b_g[i - 4] : kOOB);
             __builtin_amdgcn_sched_barrier(0);
@@ -361,26 +382,113 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         __builtin_amdgcn_sched_barrier(0);
         // second half: MFMAs of k-slice 1 (set 1) with the reads of step kt+1's k-slice 0
         // (set 0) and the refill of this step's buffer for step kt+4
-        const int s1 = (kt + 1) & (NSTAGE - 1);
-        const int k0 = (kt + NSTAGE) * BK;
-        const bool a_ok = (k0 + a_kc * 8) < Ke;
-        const uint32_t a_dst = a_dst0 + (uint32_t)s * STAGE;
-        const uint32_t a_off = a_g0 + (uint32_t)k0 * 2u;
+        // refill: half 1 - kt%2 of slab (kt+5)/2 (its buffer's slab, (kt+5)/2 - 3, was last
+        // read by steps kt-1 and kt, both finished at the barrier above)
+        const int slab = (kt + 5) >> 1, h = 1 - (kt & 1);
+        const int ka = 64 * slab;
+        const uint32_t a_dst = lds_base + (uint32_t)((slab % 3) * A_SLAB) +
+                               (uint32_t)((16 * h + 4 * (int)wave_u) * 1024);
+        const uint32_t a_off = (uint32_t)h * a_hstep + (uint32_t)ka * 2u;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             mfma_item(1, i);
-            if (NX && i < 12) read_item(s1, 0, 0, i);
+            if (NX && i < 12) read_item(kt + 1, 0, 0, i);
             if (RA && i < 4)
-                lds_dma16_at(rA, a_dst + i * 1024u, a_ok ? a_off + (uint32_t)i * a_gstep : kOOB);
+                lds_dma16_at(rA, a_dst + i * 1024u,
+                             (ka + a_c[i] * 8) < Ke ? a_g[i] + a_off : kOOB);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    // Fast steps (tiles wholly inside M, loads wholly inside K): twelve steps per iteration (the
+    // period of the four B stages and the three A slabs of two steps), so every LDS address is a
+    // constant; B's resource keeps the maximum record count and only its base moves; A's loads
+    // keep their lane offsets and take the slab's k offset and half in the scalar offset.
+    uint32_t fb_lo = 0, fb_hi = 0, fa0 = 0, fa1 = 0;
+    const uint64_t fb_step = (uint64_t)BK * (uint64_t)N * 2u;
+    const uint32_t fbs_lo = (uint32_t)fb_step, fbs_hi = (uint32_t)(fb_step >> 32);
+    const uint32_t wave_lds = lds_base + wave_u * 4096u;
+    uint32_t b_vo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b_vo[j] = b_ok[j] ? b_g[j] : kOOB;
+    auto step_fast = [&](auto r_c) {
+        constexpr int R = decltype(r_c)::value;            // kt mod 12
+        constexpr int S3 = (R + NSTAGE - 1) & (NSTAGE - 1);
+        constexpr uint32_t B_DST3 = (uint32_t)(B_REGION + S3 * B_STAGE);
+        constexpr int SLAB = (R + 5) >> 1, H = 1 - (R & 1);
+        constexpr uint32_t A_DST = (uint32_t)((SLAB % 3) * A_SLAB + 16 * H * 1024);
+        constexpr uint32_t A_K = (uint32_t)(128 * SLAB);     // slab k offset in bytes, this group
+        i32x4_t rBf;
+        rBf.x = (int)fb_lo;
+        rBf.y = (int)fb_hi;
+        rBf.z = (int)kMaxRecords;
+        rBf.w = kRsrcWord3;
+        uint32_t a_so = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            mfma_item(0, i);
+            if (i < 12) read_item(R, 1, 1, i);
+            if (i == 4) lds_dma16_so<B_DST3 + 0u>(rBf, wave_lds, b_vo[0], 0u);
+            if (i == 5) lds_dma16_so<B_DST3 + 1024u>(rBf, wave_lds, b_vo[1], 0u);
+            if (i == 6) lds_dma16_so<B_DST3 + 2048u>(rBf, wave_lds, b_vo[2], 0u);
+            if (i == 7) lds_dma16_so<B_DST3 + 3072u>(rBf, wave_lds, b_vo[3], 0u);
+            if (i == 12)
+                asm volatile("s_add_u32 %0, %1, %2" : "=s"(a_so) : "s"(H ? fa1 : fa0), "n"(A_K) : "scc");
+            if (i == 13)
+                asm volatile("s_add_u32 %0, %0, %2\n\ts_addc_u32 %1, %1, %3"
+                             : "+s"(fb_lo), "+s"(fb_hi)
+                             : "s"(fbs_lo), "s"(fbs_hi)
+                             : "scc");
+            if (R == 11 && i == 14)
+                asm volatile("s_add_u32 %0, %0, %2\n\ts_add_u32 %1, %1, %2"
+                             : "+s"(fa0), "+s"(fa1)
+                             : "n"(128 * 6)
+                             : "scc");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        C3_WAIT_VMCNT(2 * LOADS_PER_STAGE);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            mfma_item(1, i);
+            if (i < 12) read_item(R + 1, 0, 0, i);
+            if (i == 0) lds_dma16_so<A_DST + 0u>(rA, wave_lds, a_g[0], a_so);
+            if (i == 1) lds_dma16_so<A_DST + 1024u>(rA, wave_lds, a_g[1], a_so);
+            if (i == 2) lds_dma16_so<A_DST + 2048u>(rA, wave_lds, a_g[2], a_so);
+            if (i == 3) lds_dma16_so<A_DST + 3072u>(rA, wave_lds, a_g[3], a_so);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     using T = std::true_type;
     using F = std::false_type;
 
 #pragma unroll
     for (int j = 0; j < 12; ++j) read_item(0, 0, 0, j);
     int kt = 0;
+    const int nkf = Ke / BK;
+    if (m0 + BM <= M && kt + 18 <= nkf) {
+        const uint64_t b0 = (uint64_t)(uintptr_t)(B + (size_t)(kt + NSTAGE - 1) * BK * N + n0);
+        fb_lo = (uint32_t)b0;
+        fb_hi = (uint32_t)(b0 >> 32);
+        fa0 = 0u;
+        fa1 = a_hstep;
+        for (; kt + 18 <= nkf; kt += 12) {
+            step_fast(std::integral_constant<int, 0>{});
+            step_fast(std::integral_constant<int, 1>{});
+            step_fast(std::integral_constant<int, 2>{});
+            step_fast(std::integral_constant<int, 3>{});
+            step_fast(std::integral_constant<int, 4>{});
+            step_fast(std::integral_constant<int, 5>{});
+            step_fast(std::integral_constant<int, 6>{});
+            step_fast(std::integral_constant<int, 7>{});
+            step_fast(std::integral_constant<int, 8>{});
+            step_fast(std::integral_constant<int, 9>{});
+            step_fast(std::integral_constant<int, 10>{});
+            step_fast(std::integral_constant<int, 11>{});
+        }
+    }
     for (; kt + NSTAGE < nk; ++kt) step(kt, T{}, T{}, T{});
     if (kt + NSTAGE - 1 < nk) {
         step(kt, T{}, F{}, T{});
