@@ -180,6 +180,27 @@ def test_gemm_split_k(c3gpu, M, N, K, monkeypatch):
     np.testing.assert_array_equal(run_gemm(c3gpu, Ai, Bi), oracle.gemm_f32acc(Ai, Bi))
 
 
+@pytest.mark.parametrize("M,N,K,splits", [
+    (520, 264, 4136, 1),    # two full tile rows + a partial one; K tail of 8 after 129 full steps
+    (520, 264, 4136, 2),    # splits of 2080 and 2056 k: unrolled main loop, then general steps
+    (256, 520, 8200, 3),    # one tile row, ragged N, splits of 2752 / 2752 / 2696 k
+    (768, 256, 1216, 1),    # exactly 38 steps: two unrolled groups of twelve, 14 general
+])
+def test_gemm_unrolled_loop_edges(c3gpu, M, N, K, splits, monkeypatch):
+    """The tile kernel's unrolled main loop (full tiles, twelve K steps at a time while every load
+    stays inside K) next to the general step (partial tiles, the last steps, ragged K), with and
+    without K split: bit-exact on integer-valued operands, within the bar on normal ones."""
+    print(f"unrolled-loop GEMM {M}x{N}x{K} splits={splits}", flush=True)
+    monkeypatch.setenv("C3_GEMM_TILE", "256")
+    monkeypatch.setenv("C3_GEMM_SPLITS", str(splits))
+    Ai = wl.gen_small_int_bf16((M, K), 8010 + K)
+    Bi = wl.gen_small_int_bf16((K, N), 8011 + N)
+    np.testing.assert_array_equal(run_gemm(c3gpu, Ai, Bi), oracle.gemm_f32acc(Ai, Bi))
+    A = wl.gen_bf16((M, K), ("normal", 0.0, 1.0), 8020 + M)
+    B = wl.gen_bf16((K, N), ("normal", 0.0, 0.02), 8021 + N)
+    check_tol(oracle.gemm_f64acc(A, B), run_gemm(c3gpu, A, B))
+
+
 @pytest.mark.parametrize("M,N,K", [(128, 128, 32), (300, 264, 72), (1000, 2000, 1000),
                                    (65, 520, 328), (1024, 776, 1040), (129, 8, 8)])
 def test_gemm_tile128(c3gpu, M, N, K, monkeypatch):
