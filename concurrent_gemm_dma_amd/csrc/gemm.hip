@@ -637,10 +637,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tile128_dma(
     else C3_WAIT_VMCNT(0);
     __builtin_amdgcn_s_barrier();
 
-    for (int kt = 0; kt < nk; ++kt) {
-        // refill the buffer step kt-1 used (every wave finished it before the last barrier)
-        if (kt + NSTAGE - 1 < nk) issue_stage((kt + NSTAGE - 1) * BK, (kt + NSTAGE - 1) & (NSTAGE - 1));
-        const char* As = smem + (kt & (NSTAGE - 1)) * STAGE;
+    auto compute = [&](const char* As) {
         const char* Bs = As + A_STAGE;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -657,6 +654,64 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_tile128_dma(
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowop[ni], colop[mi],
                                                                           acc[mi][ni], 0, 0, 0);
         }
+    };
+
+    // Fast steps (as in the 256 kernel): while the refill of step kt+3 lies wholly inside K,
+    // four steps per iteration, one per stage, so that stage addresses are constants; A's lane
+    // offsets stay fixed and the k offset rides in the scalar offset; B's resource keeps the
+    // maximum record count and only its base moves. Per step that leaves four loads, the twelve
+    // LDS reads, eight MFMAs and two scalar updates, instead of the general step's per-step
+    // resource, address and branch work.
+    int kt = 0;
+    const int nkf = K / BK;
+    if (kt + 7 <= nkf) {
+        const uint32_t lds_base = (uint32_t)(uintptr_t)(C3_LDS char*)smem;
+        const uint32_t wave_lds = lds_base + __builtin_amdgcn_readfirstlane((uint32_t)wave) * 2048u;
+        uint32_t a_vo[2], b_vo[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            a_vo[j] = a_g0 + (uint32_t)j * a_gstep;
+            b_vo[j] = b_ok[j] ? b_g[j] : kOOB;
+        }
+        const uint64_t b0 = (uint64_t)(uintptr_t)(B + (size_t)(NSTAGE - 1) * BK * N + n0);
+        uint32_t fb_lo = (uint32_t)b0, fb_hi = (uint32_t)(b0 >> 32);
+        uint32_t fa_so = (uint32_t)(NSTAGE - 1) * BK * 2u;
+        const uint64_t fb_step = (uint64_t)BK * (uint64_t)N * 2u;
+        const uint32_t fbs_lo = (uint32_t)fb_step, fbs_hi = (uint32_t)(fb_step >> 32);
+        auto step_fast = [&](auto s_c) {
+            constexpr int S = decltype(s_c)::value;
+            constexpr uint32_t DST = (uint32_t)(((S + NSTAGE - 1) & (NSTAGE - 1)) * STAGE);
+            i32x4_t rBf;
+            rBf.x = (int)fb_lo;
+            rBf.y = (int)fb_hi;
+            rBf.z = (int)kMaxRecords;
+            rBf.w = kRsrcWord3;
+            lds_dma16_so<DST + 0u>(rA, wave_lds, a_vo[0], fa_so);
+            lds_dma16_so<DST + 1024u>(rA, wave_lds, a_vo[1], fa_so);
+            lds_dma16_so<DST + A_STAGE + 0u>(rBf, wave_lds, b_vo[0], 0u);
+            lds_dma16_so<DST + A_STAGE + 1024u>(rBf, wave_lds, b_vo[1], 0u);
+            asm volatile("s_add_u32 %0, %0, %1" : "+s"(fa_so) : "n"(BK * 2) : "scc");
+            asm volatile("s_add_u32 %0, %0, %2\n\ts_addc_u32 %1, %1, %3"
+                         : "+s"(fb_lo), "+s"(fb_hi)
+                         : "s"(fbs_lo), "s"(fbs_hi)
+                         : "scc");
+            compute(smem + S * STAGE);
+            C3_WAIT_VMCNT(8);                    // step kt+1 landed (kt+2, kt+3 in flight)
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+        };
+        for (; kt + 7 <= nkf; kt += 4) {
+            step_fast(std::integral_constant<int, 0>{});
+            step_fast(std::integral_constant<int, 1>{});
+            step_fast(std::integral_constant<int, 2>{});
+            step_fast(std::integral_constant<int, 3>{});
+        }
+    }
+
+    for (; kt < nk; ++kt) {
+        // refill the buffer step kt-1 used (every wave finished it before the last barrier)
+        if (kt + NSTAGE - 1 < nk) issue_stage((kt + NSTAGE - 1) * BK, (kt + NSTAGE - 1) & (NSTAGE - 1));
+        compute(smem + (kt & (NSTAGE - 1)) * STAGE);
         // step kt+1 landed for this wave (stages kt+2, kt+3 may be in flight); this wave's
         // reads of step kt are done; then every wave is past both points
         const int g = min(max(nk - kt - 2, 0), NSTAGE - 2);
@@ -905,13 +960,13 @@ int env_int(const char* name, int dflt) {
 }
 
 // K splits for the tile kernel from a cost model, in microseconds, measured on MI355X: a 32-deep
-// K step of a 256x256 tile takes about 0.85 us on one CU; with splits, the fp32 partials are
+// K step of a 256x256 tile takes about 0.77 us on one CU; with splits, the fp32 partials are
 // written and read back at about 3.5 TB/s and the reduction launch adds about 4 us. Time of s
-// splits = waves * steps per split * 0.85 (+ partial traffic + 4 if s > 1); the smallest wins,
+// splits = waves * steps per split * 0.77 (+ partial traffic + 4 if s > 1); the smallest wins,
 // ties to fewer splits. With at least as many tiles as CUs this is always 1.
 int choose_splits(int64_t M, int64_t N, int64_t K, int tiles, int n_cu, int max_splits,
                   double* t_out) {
-    constexpr double kStepUs = 0.85, kPartialBytesPerUs = 3.5e6, kReduceLaunchUs = 4.0;
+    constexpr double kStepUs = 0.77, kPartialBytesPerUs = 3.5e6, kReduceLaunchUs = 4.0;
     int best = 1;
     double best_t = 0.0;
     for (int s = 1; s <= max_splits; ++s) {
@@ -931,13 +986,16 @@ int choose_splits(int64_t M, int64_t N, int64_t K, int tiles, int n_cu, int max_
     return best;
 }
 
-// Time of the 128x128 tile kernel in the same units: two workgroups per CU, about 0.6 us per
-// 32-deep K step of a workgroup (measured on MI355X for 64-576 tiles of 128x128).
+// Time of the 128x128 tile kernel in the same units (measured on MI355X for 64-512 tiles of
+// 128x128): a 32-deep K step takes about 0.5 us with one workgroup on a CU and about 0.62 us
+// for each of two sharing one.
 double tile128_time(int64_t M, int64_t N, int64_t K, int n_cu) {
-    constexpr double kStepUs = 0.6;
+    constexpr double kStepAloneUs = 0.5, kStepSharedUs = 0.62;
     const int64_t tiles = ((M + tq::BM - 1) / tq::BM) * ((N + tq::BN - 1) / tq::BN);
+    const double steps = (double)((K + tq::BK - 1) / tq::BK);
+    if (tiles <= n_cu) return steps * kStepAloneUs;
     const int64_t waves = (tiles + 2 * n_cu - 1) / (2 * n_cu);
-    return (double)waves * (double)((K + tq::BK - 1) / tq::BK) * kStepUs;
+    return (double)waves * steps * kStepSharedUs;
 }
 
 }  // namespace
