@@ -402,7 +402,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     // Fast steps (tiles wholly inside M, loads wholly inside K): twelve steps per iteration (the
     // period of the four B stages and the three A slabs of two steps), so every LDS address is a
     // constant; B's resource keeps the maximum record count and only its base moves; A's loads
-    // keep their lane offsets and take the slab's k offset and half in the scalar offset.
+    // keep their lane offsets and take the slab's k offset and half in the scalar offset (fa0 /
+    // fa1: the group's k offset for rows 0..127 / 128..255, advanced by six slabs per group).
+    // With one wave per SIMD a wave issues at most one instruction every four cycles, so a
+    // 32-cycle MFMA covers seven others; the few scalar updates left sit in slots that issue
+    // nothing else, which keeps every slot at five non-MFMA instructions or fewer.
     uint32_t fb_lo = 0, fb_hi = 0, fa0 = 0, fa1 = 0;
     const uint64_t fb_step = (uint64_t)BK * (uint64_t)N * 2u;
     const uint32_t fbs_lo = (uint32_t)fb_step, fbs_hi = (uint32_t)(fb_step >> 32);
@@ -416,7 +420,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         constexpr uint32_t B_DST3 = (uint32_t)(B_REGION + S3 * B_STAGE);
         constexpr int SLAB = (R + 5) >> 1, H = 1 - (R & 1);
         constexpr uint32_t A_DST = (uint32_t)((SLAB % 3) * A_SLAB + 16 * H * 1024);
-        constexpr uint32_t A_K = (uint32_t)(128 * SLAB);     // slab k offset in bytes, this group
+        constexpr uint32_t A_K = (uint32_t)(128 * SLAB);     // slab's k offset within the group, bytes
         i32x4_t rBf;
         rBf.x = (int)fb_lo;
         rBf.y = (int)fb_hi;
