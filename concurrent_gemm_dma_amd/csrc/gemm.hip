@@ -402,18 +402,22 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     // Fast steps (tiles wholly inside M, loads wholly inside K): twelve steps per iteration (the
     // period of the four B stages and the three A slabs of two steps), so every LDS address is a
     // constant; B's resource keeps the maximum record count and only its base moves; A's loads
-    // keep their lane offsets and take the slab's k offset and half in the scalar offset (fa0 /
-    // fa1: the group's k offset for rows 0..127 / 128..255, advanced by six slabs per group).
+    // keep their lane offsets (one set per half of the rows, so that rows past M stay out of
+    // range in the lane offset itself) and take the slab's k offset in the scalar offset (fa0:
+    // the group's k offset, advanced by six slabs per group).
     // With one wave per SIMD a wave issues at most one instruction every four cycles, so a
     // 32-cycle MFMA covers seven others; the few scalar updates left sit in slots that issue
     // nothing else, which keeps every slot at five non-MFMA instructions or fewer.
-    uint32_t fb_lo = 0, fb_hi = 0, fa0 = 0, fa1 = 0;
+    uint32_t fb_lo = 0, fb_hi = 0, fa0 = 0;
     const uint64_t fb_step = (uint64_t)BK * (uint64_t)N * 2u;
     const uint32_t fbs_lo = (uint32_t)fb_step, fbs_hi = (uint32_t)(fb_step >> 32);
     const uint32_t wave_lds = lds_base + wave_u * 4096u;
-    uint32_t b_vo[4];
+    uint32_t b_vo[4], a_vo1[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b_vo[j] = b_ok[j] ? b_g[j] : kOOB;
+    for (int j = 0; j < 4; ++j) {
+        b_vo[j] = b_ok[j] ? b_g[j] : kOOB;
+        a_vo1[j] = a_g[j] + a_hstep;
+    }
     auto step_fast = [&](auto r_c) {
         constexpr int R = decltype(r_c)::value;            // kt mod 12
         constexpr int S3 = (R + NSTAGE - 1) & (NSTAGE - 1);
@@ -436,17 +440,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
             if (i == 6) lds_dma16_so<B_DST3 + 2048u>(rBf, wave_lds, b_vo[2], 0u);
             if (i == 7) lds_dma16_so<B_DST3 + 3072u>(rBf, wave_lds, b_vo[3], 0u);
             if (i == 12)
-                asm volatile("s_add_u32 %0, %1, %2" : "=s"(a_so) : "s"(H ? fa1 : fa0), "n"(A_K) : "scc");
+                asm volatile("s_add_u32 %0, %1, %2" : "=s"(a_so) : "s"(fa0), "n"(A_K) : "scc");
             if (i == 13)
                 asm volatile("s_add_u32 %0, %0, %2\n\ts_addc_u32 %1, %1, %3"
                              : "+s"(fb_lo), "+s"(fb_hi)
                              : "s"(fbs_lo), "s"(fbs_hi)
                              : "scc");
             if (R == 11 && i == 14)
-                asm volatile("s_add_u32 %0, %0, %2\n\ts_add_u32 %1, %1, %2"
-                             : "+s"(fa0), "+s"(fa1)
-                             : "n"(128 * 6)
-                             : "scc");
+                asm volatile("s_add_u32 %0, %0, %1" : "+s"(fa0) : "n"(128 * 6) : "scc");
             __builtin_amdgcn_sched_barrier(0);
         }
         C3_WAIT_VMCNT(2 * LOADS_PER_STAGE);
@@ -457,10 +458,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         for (int i = 0; i < 16; ++i) {
             mfma_item(1, i);
             if (i < 12) read_item(R + 1, 0, 0, i);
-            if (i == 0) lds_dma16_so<A_DST + 0u>(rA, wave_lds, a_g[0], a_so);
-            if (i == 1) lds_dma16_so<A_DST + 1024u>(rA, wave_lds, a_g[1], a_so);
-            if (i == 2) lds_dma16_so<A_DST + 2048u>(rA, wave_lds, a_g[2], a_so);
-            if (i == 3) lds_dma16_so<A_DST + 3072u>(rA, wave_lds, a_g[3], a_so);
+            if (i == 0) lds_dma16_so<A_DST + 0u>(rA, wave_lds, H ? a_vo1[0] : a_g[0], a_so);
+            if (i == 1) lds_dma16_so<A_DST + 1024u>(rA, wave_lds, H ? a_vo1[1] : a_g[1], a_so);
+            if (i == 2) lds_dma16_so<A_DST + 2048u>(rA, wave_lds, H ? a_vo1[2] : a_g[2], a_so);
+            if (i == 3) lds_dma16_so<A_DST + 3072u>(rA, wave_lds, H ? a_vo1[3] : a_g[3], a_so);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -472,12 +473,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     for (int j = 0; j < 12; ++j) read_item(0, 0, 0, j);
     int kt = 0;
     const int nkf = Ke / BK;
-    if (m0 + BM <= M && kt + 18 <= nkf) {
+    if (kt + 18 <= nkf) {
         const uint64_t b0 = (uint64_t)(uintptr_t)(B + (size_t)(kt + NSTAGE - 1) * BK * N + n0);
         fb_lo = (uint32_t)b0;
         fb_hi = (uint32_t)(b0 >> 32);
         fa0 = 0u;
-        fa1 = a_hstep;
         for (; kt + 18 <= nkf; kt += 12) {
             step_fast(std::integral_constant<int, 0>{});
             step_fast(std::integral_constant<int, 1>{});
