@@ -399,7 +399,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    // Fast steps (tiles wholly inside M, loads wholly inside K): twelve steps per iteration (the
+    // Fast steps (while every load they issue lies wholly inside K): twelve steps per iteration (the
     // period of the four B stages and the three A slabs of two steps), so every LDS address is a
     // constant; B's resource keeps the maximum record count and only its base moves; A's loads
     // keep their lane offsets (one set per half of the rows, so that rows past M stay out of
