@@ -201,6 +201,35 @@ def test_gemm_unrolled_loop_edges(c3gpu, M, N, K, splits, monkeypatch):
     check_tol(oracle.gemm_f64acc(A, B), run_gemm(c3gpu, A, B))
 
 
+@pytest.mark.parametrize("M,N,K,tile,splits", [
+    (300, 520, 1000, "256", "1"),   # 256 tile: partial tile rows and columns, K tail of 8
+    (520, 264, 4136, "256", "2"),   # 256 tile, K split: each split's own tail
+    (300, 520, 1000, "128", "0"),   # 128 tile
+    (40, 520, 1000, "0", "0"),      # skinny
+])
+def test_gemm_reads_and_writes_only_its_operands(c3gpu, M, N, K, tile, splits, monkeypatch):
+    """Every operand is followed in memory by NaN (A, B) or a sentinel (C), with room for any
+    over-read or over-write a missing mask could make (a tile of rows past M, a K step past K):
+    C must still equal the exact result, which any NaN read into a sum would break, and the
+    sentinel after C must be untouched."""
+    import torch
+
+    print(f"operand-bounds GEMM {M}x{N}x{K} tile={tile} splits={splits}", flush=True)
+    monkeypatch.setenv("C3_GEMM_TILE", tile)
+    monkeypatch.setenv("C3_GEMM_SPLITS", splits)
+    A = wl.gen_small_int_bf16((M, K), 8100 + K)
+    B = wl.gen_small_int_bf16((K, N), 8101 + N)
+    nan = np.uint16(0x7FC0)
+    dA = to_dev(np.concatenate([A.reshape(-1), np.full(256 * K + 64, nan, np.uint16)]))
+    dB = to_dev(np.concatenate([B.reshape(-1), np.full(32 * N + 64, nan, np.uint16)]))
+    dC = empty_bf16((M * N + 256 * N,), fill=0x1234)
+    c3gpu.c3_gemm(dA, dB, dC, M, N, K, None)
+    torch.cuda.synchronize()
+    out = bf16_from_dev(dC)
+    np.testing.assert_array_equal(out[:M * N].reshape(M, N), oracle.gemm_f32acc(A, B))
+    assert np.all(out[M * N:] == 0x1234)
+
+
 @pytest.mark.parametrize("M,N,K", [(128, 128, 32), (300, 264, 72), (1000, 2000, 1000),
                                    (65, 520, 328), (1024, 776, 1040), (129, 8, 8)])
 def test_gemm_tile128(c3gpu, M, N, K, monkeypatch):
