@@ -39,6 +39,7 @@ C3_FAULT_ERROR_CHUNK = 3
 C3_MAX_MASK_WORDS = 8
 C3_MAX_WORLD = 64
 C3_MAX_CURVE = 16
+C3_ABI_VERSION = 4
 TAXONOMY = {0: "GC-equal", 1: "G-long", 2: "C-long"}
 
 # Every symbol include/c3.h declares.
@@ -107,10 +108,15 @@ class c3_timing(ctypes.Structure):
                 ("sdma_first_start_ns", ctypes.c_int64), ("sdma_last_end_ns", ctypes.c_int64),
                 ("n_chunks", ctypes.c_int32), ("engines_used", ctypes.c_uint32),
                 ("applied_priority", ctypes.c_int32), ("comm_issued_first", ctypes.c_int32),
-                ("t_reduce_done_ns", ctypes.c_int64), ("reduce_gpu_ms", ctypes.c_double)]
+                ("t_reduce_done_ns", ctypes.c_int64), ("reduce_gpu_ms", ctypes.c_double),
+                ("gemm_applied_mask", ctypes.c_uint32 * C3_MAX_MASK_WORDS),
+                ("comm_applied_mask", ctypes.c_uint32 * C3_MAX_MASK_WORDS)]
 
     def as_dict(self):
-        return {n: getattr(self, n) for n, _ in self._fields_}
+        d = {n: getattr(self, n) for n, _ in self._fields_}
+        for n in ("gemm_applied_mask", "comm_applied_mask"):
+            d[n] = list(d[n])
+        return d
 
 
 class c3_metrics(ctypes.Structure):

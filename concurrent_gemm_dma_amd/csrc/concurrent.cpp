@@ -362,6 +362,14 @@ c3_status run_concurrent(const c3_gemm_args* g, const c3_copy_args* c, const c3_
     t.t_issue_ns = t_issue;
     t.applied_priority = 0;
     t.comm_issued_first = (c && o.comm_first) ? 1 : 0;
+    if (g) {
+        const auto m = normalise(o.gemm_cu_mask, C3_MAX_MASK_WORDS);
+        std::copy(m.begin(), m.end(), t.gemm_applied_mask);
+    }
+    if (need_cs) {
+        const auto m = normalise(o.comm_cu_mask, C3_MAX_MASK_WORDS);
+        std::copy(m.begin(), m.end(), t.comm_applied_mask);
+    }
     if (gemm_issued) {
         float ms = 0.f;
         if (hipEventElapsedTime(&ms, ev.g0, ev.g1) == hipSuccess) t.gemm_gpu_ms = ms;

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define C3_ABI_VERSION 3
+#define C3_ABI_VERSION 4
 #define C3_MAX_MASK_WORDS 8 /* CU masks cover up to 256 CUs, bit i = CU i as the driver numbers it */
 #define C3_MAX_SEGMENTS 4096
 #define C3_MAX_WORLD 64 /* ranks of a reduce-scatter / all-reduce local share */
@@ -179,6 +179,12 @@ typedef struct {
     int32_t comm_issued_first;
     int64_t t_reduce_done_ns;/* all-reduce: first issue -> reduce-scatter completion observed */
     double reduce_gpu_ms;    /* all-reduce: HIP events around the reduce-scatter kernel(s) */
+    /* CU masks the run actually applied, after normalisation (an all-zero request becomes every
+     * CU of the device; bits past the device's last CU are dropped). gemm_applied_mask is the
+     * GEMM stream's mask (all zero when no GEMM ran); comm_applied_mask is the communication
+     * stream's (all zero when no kernel of the copy ran on the CUs, e.g. a pure SDMA copy). */
+    uint32_t gemm_applied_mask[C3_MAX_MASK_WORDS];
+    uint32_t comm_applied_mask[C3_MAX_MASK_WORDS];
 } c3_timing;
 
 #define C3_MAX_CURVE 16

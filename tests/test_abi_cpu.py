@@ -88,7 +88,7 @@ def test_struct_sizes_match_header_layout(c3):
     assert ctypes.sizeof(c3.c3_gemm_args) == 48
     assert ctypes.sizeof(c3.c3_copy_args) == 56 + 40 + 24
     assert ctypes.sizeof(c3.c3_conc_opts) == 32 + 32 + 8 + 8
-    assert ctypes.sizeof(c3.c3_timing) == 8 * 8 + 16 + 16
+    assert ctypes.sizeof(c3.c3_timing) == 8 * 8 + 16 + 16 + 2 * 4 * c3.C3_MAX_MASK_WORDS
     assert ctypes.sizeof(c3.c3_metrics) == 6 * 8 + 8
     assert ctypes.sizeof(c3.c3_info) == 12 * 4 + 8 + 64
 

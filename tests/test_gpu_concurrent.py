@@ -155,6 +155,16 @@ class Case:
             assert oracle.first_diff(self.want_reduced, bytes_from_dev(self.reduced)) == -1, label
 
 
+def applied(mask, n_cu):
+    """The mask a run applies for a requested one: None means every CU of the device."""
+    if mask is None:
+        words = [0] * 8
+        for b in range(n_cu):
+            words[b // 32] |= 1 << (b % 32)
+        return words
+    return [int(w) for w in mask]
+
+
 def run_cells(c3, case, cells):
     # isolated GEMM (the reference bits for every concurrent cell)
     case.poison(0)
@@ -179,6 +189,12 @@ def run_cells(c3, case, cells):
         assert t["t_conc_ns"] > 0 and t["t_conc_ns"] >= max(t["t_gemm_done_ns"], t["t_copy_done_ns"])
         assert t["comm_issued_first"] == int(comm_first)
         assert t["applied_priority"] == 0
+        # the masks the run reports are the ones it was given (all CUs for "no mask"); a pure
+        # SDMA gather or all-to-all runs no kernel on the communication stream
+        assert t["gemm_applied_mask"] == applied(gm, info["n_cu"]), label
+        comm_on_cus = mover == "cu" or case.copy == "allreduce"
+        assert t["comm_applied_mask"] == (applied(cm, info["n_cu"]) if comm_on_cus
+                                          else [0] * c3.C3_MAX_MASK_WORDS), label
         if mover == "sdma":
             assert t["engines_used"] != 0 and t["n_chunks"] >= 1
         if case.copy == "allreduce":

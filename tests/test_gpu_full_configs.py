@@ -2,7 +2,14 @@
 (c3_run_concurrent; SDMA, CU and hybrid movers): the whole copy destination byte-exact (for the
 all-reduce: the whole reduced chunk and the whole gathered output bit-exact), the GEMM checked on
 sampled outputs (random elements, corners, a full row and a full column) against the oracle,
-and bit-exact at full shape with small-integer operands (where the result is unique)."""
+and bit-exact at full shape with small-integer operands (where the result is unique).
+
+Every concurrent cell's C must also be bit-identical to the GEMM's isolated run. The GC-equal
+workload (4096x16384x8192 beside an 8-shard gather) runs its whole grid at full size: mover
+{CU, SDMA} x GEMM CUs per XCC {all, 7/8, 3/4} (a CU-mover copy gets the complement, the SDMA
+mover leaves it idle) x {communication first, GEMM first} (Section V-B and Fig. 8 of the paper
+for the two controls; the Pith review's referee comment on Section V-B and its suggested test
+of checking every buffer after each concurrent run)."""
 import numpy as np
 import pytest
 
@@ -20,7 +27,11 @@ def sync():
     torch.cuda.synchronize()
 
 
-def run_workload(c3, w, int_exact=False, movers=("sdma", "cu"), n_samples=1024):
+def run_workload(c3, w, int_exact=False, movers=("sdma", "cu"), n_samples=1024, cells=None):
+    """cells: (mover, GEMM CUs per XCC or None for all, comm_first) tuples; by default every
+    mover of `movers` on all CUs, communication first."""
+    if cells is None:
+        cells = [(m, None, True) for m in movers]
     A, B = wl.gen_gemm_operands(w, int_exact=int_exact)
     dA, dB = to_dev(A), to_dev(B)
     dC = empty_bf16((w.M, w.N))
@@ -46,8 +57,24 @@ def run_workload(c3, w, int_exact=False, movers=("sdma", "cu"), n_samples=1024):
     rows, cols = wl.sample_indices(w.M, w.N, n_samples, seed=w.wid, full_rows=(w.M // 3,),
                                    full_cols=(w.N - 1,))
     c32, c64, _ = oracle.gemm_elems(A, B, rows, cols)
-    first_c = None
-    for r, mover in enumerate(movers):
+
+    def check_sampled(got, label):
+        sampled = got[rows, cols]
+        if int_exact:
+            np.testing.assert_array_equal(sampled, c32, err_msg=label)
+        else:
+            for ref in (c64, c32):
+                rep = oracle.gemm_compare(ref, sampled)
+                assert oracle.gemm_within_tolerance(rep), (label, rep)
+
+    # the isolated GEMM: the bits every concurrent cell must reproduce
+    dC.fill_(-1)
+    sync()
+    c3.c3_run_concurrent(c3.gemm_args(dA, dB, dC, w.M, w.N, w.K), None)
+    iso_c = bf16_from_dev(dC)
+    check_sampled(iso_c, "isolated")
+    info = c3.c3_device_info()
+    for r, (mover, keep, comm_first) in enumerate(cells, start=1):
         dC.fill_(-1 - r)
         dst.fill_(0x5A + r)
         if reduced is not None:
@@ -65,27 +92,30 @@ def run_workload(c3, w, int_exact=False, movers=("sdma", "cu"), n_samples=1024):
                                              w.unit_bytes, m, opts)
         else:
             cargs, _keep = c3.all2all_args(dst, src, w.units, w.unit_bytes, m, opts)
+        gm = cm = None
+        if keep is not None:
+            gm = c3.c3_cu_mask_balanced(keep)
+            if m != c3.C3_MOVER_SDMA:
+                cm = c3.c3_cu_mask_balanced(keep, complement=True)
+        label = (f"workload {w.wid} ({w.name}, copy {w.copy_bytes // MiB} MiB) mover={mover} "
+                 f"gemm_cus_per_xcc={keep or 'all'} "
+                 f"{'comm-first' if comm_first else 'gemm-first'} int_exact={int_exact}")
+        print(label, flush=True)
         t = c3.c3_run_concurrent(c3.gemm_args(dA, dB, dC, w.M, w.N, w.K), cargs,
-                                 c3.conc_opts(comm_first=True))
-        print(f"workload {w.wid} ({w.name}) mover={mover} int_exact={int_exact}: "
-              f"t_conc={t['t_conc_ns'] / 1e6:.3f} ms", flush=True)
-        assert oracle.first_diff(want, bytes_from_dev(dst)) == -1, f"copy mismatch ({mover})"
+                                 c3.conc_opts(gemm_mask=gm, comm_mask=cm, comm_first=comm_first))
+        print(f"  t_conc={t['t_conc_ns'] / 1e6:.3f} ms", flush=True)
+        assert t["comm_issued_first"] == int(comm_first)
+        if gm is not None:
+            assert t["gemm_applied_mask"] == list(gm), label
+            assert sum(bin(x).count("1") for x in t["gemm_applied_mask"]) == keep * info["n_xcc"]
+        assert oracle.first_diff(want, bytes_from_dev(dst)) == -1, f"copy mismatch ({label})"
         if reduced is not None:
             assert oracle.first_diff(want_red, bytes_from_dev(reduced)) == -1, \
-                f"reduce-scatter mismatch ({mover})"
+                f"reduce-scatter mismatch ({label})"
         got = bf16_from_dev(dC)
-        sampled = got[rows, cols]
-        if int_exact:
-            np.testing.assert_array_equal(sampled, c32)
-        else:
-            for ref in (c64, c32):
-                rep = oracle.gemm_compare(ref, sampled)
-                assert oracle.gemm_within_tolerance(rep), rep
-        if first_c is None:
-            first_c = got
-        else:
-            np.testing.assert_array_equal(got, first_c)
-    return first_c
+        check_sampled(got, label)
+        np.testing.assert_array_equal(got, iso_c, err_msg=label)
+    return iso_c
 
 
 @pytest.mark.parametrize("wid", [1, 2, 3, 4, 6])
@@ -97,6 +127,18 @@ def test_full_workload(c3gpu, wid):
 def test_full_gc_equal_sweep_ends(c3gpu, total_mib):
     run_workload(c3gpu, wl.WORKLOADS[5].with_gather_total(total_mib * MiB),
                  movers=("sdma", "hybrid:679"))
+
+
+@pytest.mark.parametrize("total_mib", [256, 1024])
+@pytest.mark.parametrize("mover", ["cu", "sdma"])
+def test_full_gc_equal_grid(c3gpu, mover, total_mib):
+    """The GC-equal workload's grid at full size: for one mover and gather size, GEMM CUs per
+    XCC {all, 7/8, 3/4} x {communication first, GEMM first}."""
+    info = c3gpu.c3_device_info()
+    per = info["n_cu"] // info["n_xcc"]
+    cells = [(mover, keep, cf) for keep in (None, per * 7 // 8, per * 3 // 4)
+             for cf in (True, False)]
+    run_workload(c3gpu, wl.WORKLOADS[5].with_gather_total(total_mib * MiB), cells=cells)
 
 
 @pytest.mark.parametrize("wid", [2, 3])
