@@ -37,7 +37,7 @@ def test_defaults(monkeypatch):
     b = load_bench()
     monkeypatch.setattr(sys, "argv", ["bench.py"])
     a = b.parse()
-    assert (a.gpus, a.steps, a.warmup, a.mode, a.workload) == (1, 20, 3, "c3", 2)
+    assert (a.gpus, a.steps, a.warmup, a.mode, a.workload) == (1, 20, 3, "c3", 4)
     assert b.PEAK_BF16_TFLOPS == 2500.0 and b.PEAK_HBM_GBPS == 8000.0
 
 
