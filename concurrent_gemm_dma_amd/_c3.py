@@ -39,12 +39,14 @@ C3_FAULT_ERROR_CHUNK = 3
 C3_MAX_MASK_WORDS = 8
 C3_MAX_WORLD = 64
 C3_MAX_CURVE = 16
+C3_NOALLOC_SCRATCH_BYTES = 16 << 20  # c3_gemm_noalloc: fixed split-K partials per device
 C3_ABI_VERSION = 4
 TAXONOMY = {0: "GC-equal", 1: "G-long", 2: "C-long"}
 
 # Every symbol include/c3.h declares.
 EXPORTS = ("c3_init", "c3_finalize", "c3_last_error", "c3_device_info", "c3_stream_create",
            "c3_stream_destroy", "c3_cu_mask_balanced", "c3_probe_placement", "c3_gemm",
+           "c3_gemm_noalloc",
            "c3_gather", "c3_all2all_block", "c3_reduce_scatter", "c3_allreduce_local",
            "c3_flush_llc", "c3_run_concurrent", "c3_derive_metrics", "c3_roofline_time",
            "c3_predict_partition", "c3_hybrid_share")
@@ -167,6 +169,7 @@ def load(path: Optional[str] = None):
     L.c3_cu_mask_balanced.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_uint32)]
     L.c3_probe_placement.argtypes = [vp, ctypes.c_int, vp]
     L.c3_gemm.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp]
+    L.c3_gemm_noalloc.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp]
     L.c3_gather.argtypes = [vp, ctypes.POINTER(vp), ctypes.c_int, ctypes.c_size_t, ctypes.c_int,
                             ctypes.POINTER(c3_move_opts), vp]
     L.c3_all2all_block.argtypes = [vp, vp, ctypes.c_int, ctypes.c_size_t, ctypes.c_int,
@@ -273,6 +276,10 @@ def c3_probe_placement(out_dev, n_blocks: int, stream=None) -> None:
 
 def c3_gemm(A, B, C, M: int, N: int, K: int, stream=None) -> None:
     check(load().c3_gemm(_ptr(A), _ptr(B), _ptr(C), M, N, K, _stream(stream)))
+
+
+def c3_gemm_noalloc(A, B, C, M: int, N: int, K: int, stream=None) -> None:
+    check(load().c3_gemm_noalloc(_ptr(A), _ptr(B), _ptr(C), M, N, K, _stream(stream)))
 
 
 def move_opts(**kw) -> c3_move_opts:

@@ -278,6 +278,17 @@ c3_status c3_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, i
     })
 }
 
+c3_status c3_gemm_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                          void* stream) {
+    C3_ENTRY({
+        C3_TRY(require_init());
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        GemmPlan plan;
+        C3_TRY(gemm_plan(A, B, C, M, N, K, s, &plan, /*noalloc=*/true));
+        return gemm_enqueue(plan, s);
+    })
+}
+
 c3_status c3_gather(void* dst, const void* const* shards, int n_shards, size_t shard_bytes,
                     c3_mover mover, const c3_move_opts* opt, void* stream) {
     C3_ENTRY({

@@ -76,9 +76,13 @@ struct GemmPlan {
     size_t workspace_bytes = 0;
 };
 c3_status gemm_validate(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K);
-// Choose the kernel and (for split-K) make sure a workspace exists for `stream`. May allocate.
+// Choose the kernel and (for split-K) make sure a workspace exists for `stream`. May allocate,
+// unless `noalloc`: then split-K partials go to the device's fixed scratch array, and a plan
+// whose partials do not fit there is refused (C3_E_INVALID).
 c3_status gemm_plan(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                    hipStream_t stream, GemmPlan* plan);
+                    hipStream_t stream, GemmPlan* plan, bool noalloc = false);
+// Bind the fixed scratch array of `device` (must be the current device). Called by c3_init.
+c3_status gemm_scratch_bind(int device);
 // Launch only (no allocation, no synchronization).
 c3_status gemm_enqueue(const GemmPlan& plan, hipStream_t stream);
 void gemm_release_workspaces();

@@ -120,6 +120,7 @@ c3_status init_device(int hip_device) {
         d.n_xcc = (int32_t)v;
     if (d.n_xcc <= 0) d.n_xcc = 1;
     c.device = hip_device;
+    C3_TRY(gemm_scratch_bind(hip_device));
     C3_TRY(sdma_discover());
     c.inited = true;
     return C3_OK;

@@ -949,6 +949,14 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ w
 
 constexpr int64_t kMaxDim = 1 << 21;
 
+// Split-K partials of c3_gemm_noalloc: one fixed array per device, loaded with the code object
+// and held until the process ends, instead of a workspace allocated per stream. In host code the
+// name is only a stand-in: kernels get the device address bound by gemm_scratch_bind.
+constexpr size_t kScratchBytes = C3_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+constexpr int kMaxDevices = 64;
+float* g_scratch_dev[kMaxDevices] = {};
+
 struct Workspace {
     float* ptr = nullptr;
     size_t bytes = 0;
@@ -1041,8 +1049,37 @@ static c3_status ensure_workspace(hipStream_t stream, size_t need, GemmPlan* p) 
     return C3_OK;
 }
 
+// Device address of `device`'s scratch array (called at c3_init with that device current).
+c3_status gemm_scratch_bind(int device) {
+    if (device < 0 || device >= kMaxDevices)
+        return fail(C3_E_UNSUPPORTED, "device %d: the no-allocation scratch covers devices 0..%d",
+                    device, kMaxDevices - 1);
+    void* p = nullptr;
+    C3_HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(C3_E_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_dev[device] = static_cast<float*>(p);
+    return C3_OK;
+}
+
+// The split-K partials of a plan: the stream's workspace (allocated on first need), or with
+// `noalloc` the device's fixed scratch array, refused when the partials do not fit in it.
+static c3_status partials(hipStream_t stream, size_t need, bool noalloc, GemmPlan* p) {
+    if (!noalloc) return ensure_workspace(stream, need, p);
+    if (need > kScratchBytes)
+        return fail(C3_E_INVALID,
+                    "c3_gemm_noalloc: this shape splits K into %d parts whose fp32 partials need "
+                    "%zu bytes, above the %zu-byte scratch (use c3_gemm)",
+                    p->splits, need, kScratchBytes);
+    const int dev = ctx().device;
+    float* w = (dev >= 0 && dev < kMaxDevices) ? g_scratch_dev[dev] : nullptr;
+    if (!w) return fail(C3_E_NOT_INIT, "c3_gemm_noalloc: no scratch bound for device %d", dev);
+    p->workspace = w;
+    p->workspace_bytes = need;
+    return C3_OK;
+}
+
 c3_status gemm_plan(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
-                    hipStream_t stream, GemmPlan* plan) {
+                    hipStream_t stream, GemmPlan* plan, bool noalloc) {
     C3_TRY(gemm_validate(A, B, C, M, N, K));
     GemmPlan p;
     p.A = A;
@@ -1070,7 +1107,7 @@ c3_status gemm_plan(const void* A, const void* B, void* C, int64_t M, int64_t N,
         if (splits > 1) {
             const size_t mpad = (size_t)sk::BM * p.mt;
             const size_t need = (size_t)splits * mpad * (size_t)N * sizeof(float);
-            C3_TRY(ensure_workspace(stream, need, &p));
+            C3_TRY(partials(stream, need, noalloc, &p));
         }
     } else {
         p.kind = 0;
@@ -1103,7 +1140,7 @@ c3_status gemm_plan(const void* A, const void* B, void* C, int64_t M, int64_t N,
         p.k_per_split = splits > 1 ? kps : (int)K;
         if (splits > 1) {
             const size_t need = (size_t)splits * (size_t)M * (size_t)N * sizeof(float);
-            C3_TRY(ensure_workspace(stream, need, &p));
+            C3_TRY(partials(stream, need, noalloc, &p));
         }
     }
     *plan = p;

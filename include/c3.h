@@ -271,6 +271,24 @@ c3_status c3_probe_placement(void* stream, int n_blocks, uint32_t* out_dev);
 c3_status c3_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                   void* stream);
 
+/* c3_gemm for callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc. Same arguments, kernels, plan and bits as
+ * c3_gemm, but a shape whose plan splits K keeps its fp32 partials in a fixed device array of
+ * C3_NOALLOC_SCRATCH_BYTES loaded with the library (one per device, held until the process
+ * ends) instead of a workspace the library allocates. Nothing is allocated or freed, on the
+ * device or through any allocating library routine; the array needs no clearing (every partial
+ * the reduction reads is written first by the same call).
+ * Errors: as c3_gemm; C3_E_INVALID, before anything is launched, when the shape's K split needs
+ * more than C3_NOALLOC_SCRATCH_BYTES of partials (c3_last_error gives the size; c3_gemm runs
+ * it). Shapes that do not split K (every shape with at least as many 256x256 output tiles as
+ * CUs) use no scratch and have no limit.
+ * Every call on one device shares that device's array: two calls that may overlap in time on
+ * that device (different streams, or another host thread's call) race and give wrong results;
+ * order them on one stream or synchronize between them. */
+#define C3_NOALLOC_SCRATCH_BYTES (16u << 20)
+c3_status c3_gemm_noalloc(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                          void* stream);
+
 /* All-gather local share: dst[i*shard_bytes + b] = shards[i][b] for i < n_shards,
  * b < shard_bytes. `shards` is a host array of n_shards device pointers; dst is device memory of
  * n_shards*shard_bytes bytes. Any alignment and size (shard_bytes = 0 is a no-op).
