@@ -30,7 +30,8 @@ Other modes print one JSON line per measured cell:
                    CU mask x order
   --mode cus       isolated GEMM time and CU-copy GB/s under balanced CU masks
   --mode partition CU-partitioning sweep (c3_rp) over 30 GEMM x collective scenarios and the
-                   slowdown-lookup-table heuristic scored against it
+                   slowdown-lookup-table heuristic (paired and isolated calibration tables)
+                   scored against it
   --mode hybrid    the hybrid mover's concurrent time against its engine share on 8 workloads,
                    and the share c3_hybrid_share picks scored against the best of the sweep
   --mode gemm_vs_vendor  the library's GEMM against torch.matmul (hipBLASLt) on the same
@@ -719,9 +720,10 @@ def run_cus(args, c3, info):
 def run_partition(args, c3, info):
     """Resource partitioning (c3_rp): the GEMM keeps N - c CUs per XCC and a CU-mover collective
     gets the other c, for c in powers of two; the best split is the sweep's upper bound. The
-    heuristic predicts the split from a one-time slowdown lookup table (calibration kernels,
-    isolated, under each mask) and isolated times estimated by a 0.70-efficiency roofline (or,
-    second variant, measured), and is scored against the sweep: hit = same split, loss =
+    heuristic predicts the split from a one-time slowdown lookup table (calibration kernels run
+    side by side on complementary CUs, each timed to its own completion; or, the first reading,
+    each alone under each mask) and isolated times estimated by a 0.70-efficiency roofline (or
+    measured), and every combination is scored against the sweep: hit = same split, loss =
     T_conc(chosen) / T_conc(best) - 1. Every configuration of a table or a scenario is run once
     per round and rounds repeat, so clock drift hits all of them alike; medians over rounds."""
     import dataclasses
@@ -745,9 +747,10 @@ def run_partition(args, c3, info):
     def mask(keep):
         return None if keep == per else c3.c3_cu_mask_balanced(keep)
 
-    def run(g, cm, gkeep=per, ckeep=per):
+    def run(g, cm, gkeep=per, ckeep=per, done=False):
         """One verified run: GEMM alone (cm None), collective alone (g None), or both with the
-        GEMM on gkeep CUs per XCC and the collective on the complementary ckeep."""
+        GEMM on gkeep CUs per XCC and the collective on the complementary ckeep. Returns the
+        run's time, or with done=True (both kernels) when each of the two completed."""
         for x in (g, cm):
             if x is not None:
                 x.poison()
@@ -763,6 +766,8 @@ def run_partition(args, c3, info):
             cm.verify_copy("partition run")
         if g is not None:
             g.verify_c("partition run")
+        if done:
+            return t["t_gemm_done_ns"] * 1e-9, t["t_copy_done_ns"] * 1e-9
         return t["t_conc_ns"] * 1e-9
 
     def medians(cells):
@@ -775,24 +780,50 @@ def run_partition(args, c3, info):
                     out[k].append(t)
         return {k: statistics.median(v) for k, v in out.items()}
 
-    # ---- one-time lookup table from calibration kernels ----
-    calib_gemm = {"compute": gemm_w(20, 4096, 16384, 8192), "memory": gemm_w(21, 16, 28672, 8192)}
-    calib_comm = {"gather": comm_w(22, "gather", 8, 32), "all2all": comm_w(23, "all2all", 8, 4)}
+    def median_pairs(cells):
+        """cells: {key: thunk returning (a, b)}; medians of a and of b per key."""
+        out = {k: [] for k in cells}
+        for i in range(reps + 1):
+            for k, f in cells.items():
+                t = f()
+                if i:
+                    out[k].append(t)
+        return {k: (statistics.median(a for a, _ in v), statistics.median(b for _, b in v))
+                for k, v in out.items()}
+
+    # ---- one-time lookup tables from calibration kernels (shapes not among the scenarios) ----
+    # "isolated": each calibration kernel alone under each mask (the first reading of the
+    # table). "paired": each calibration GEMM and collective side by side on complementary CUs,
+    # each slowed-down time taken at its own completion, relative to the kernel alone on all CUs:
+    # a collective on few CUs beside a compute-bound GEMM runs at the clock the GEMM leaves it
+    # (the chip is power-limited), which an isolated table cannot see. Tables are per GEMM class
+    # and collective kind, so a scenario looks its pair up.
+    calib_gemm = {"compute": gemm_w(20, 8192, 16384, 8192), "memory": gemm_w(21, 32, 28672, 8192)}
+    calib_comm = {"gather": comm_w(22, "gather", 8, 16), "all2all": comm_w(23, "all2all", 8, 2)}
     tables = {}
-    for cls, w in calib_gemm.items():
-        g = Setup(c3, w, check=not args.profile, with_comm=False)
+    calib_g = {cls: Setup(c3, w, check=not args.profile, with_comm=False)
+               for cls, w in calib_gemm.items()}
+    calib_c = {kind: Setup(c3, w, with_gemm=False, check=not args.profile)
+               for kind, w in calib_comm.items()}
+    alone = {}
+    for cls, g in calib_g.items():
         for _ in range(5):  # clocks up before anything is timed
             run(g, None)
         m = medians({k: (lambda k=k: run(g, None, gkeep=k)) for k in [per] + [per - c for c in opts]})
         tables[("gemm", cls)] = {k: m[k] / m[per] for k in m if k != per}
-        del g
-    for kind, w in calib_comm.items():
-        cm = Setup(c3, w, with_gemm=False, check=not args.profile)
+        alone[cls] = m[per]
+    for kind, cm in calib_c.items():
         m = medians({k: (lambda k=k: run(None, cm, ckeep=k)) for k in [per] + opts})
         tables[("comm", kind)] = {k: m[k] / m[per] for k in m if k != per}
-        del cm
-    for (role, cls), tab in tables.items():
-        print(json.dumps({"mode": "partition", "table": f"{role}:{cls}",
+        alone[kind] = m[per]
+    for cls, g in calib_g.items():
+        for kind, cm in calib_c.items():
+            m = median_pairs({c: (lambda c=c: run(g, cm, gkeep=per - c, done=True)) for c in opts})
+            tables[("gemm", cls, kind)] = {per - c: m[c][0] / alone[cls] for c in opts}
+            tables[("comm", kind, cls)] = {c: m[c][1] / alone[kind] for c in opts}
+    del calib_g, calib_c
+    for key, tab in tables.items():
+        print(json.dumps({"mode": "partition", "table": ":".join(key),
                           "slowdown_by_cus_per_xcc": {str(k): round(v, 4) for k, v in sorted(tab.items())}}),
               flush=True)
 
@@ -803,8 +834,9 @@ def run_partition(args, c3, info):
              ("all2all", 8, 4)]
     comm_setups = [Setup(c3, comm_w(40 + i, *cdef), with_gemm=False, check=not args.profile)
                    for i, cdef in enumerate(comms)]
-    hits = {"roofline": 0, "measured": 0}
-    losses = {"roofline": [], "measured": []}
+    variants = [(t, tv) for tv in ("paired", "isolated") for t in ("measured", "roofline")]
+    hits = {v: 0 for v in variants}
+    losses = {v: [] for v in variants}
     gain_rp_over_sp = []
     n = 0
     for gi, (M, N, K) in enumerate(gemms):
@@ -825,15 +857,20 @@ def run_partition(args, c3, info):
             est_g = c3.c3_roofline_time(w.gemm_flops, w.gemm_bytes, peak_f, peak_b, eff)
             est_c = c3.c3_roofline_time(0.0, cw.comm_hbm_bytes, peak_f, peak_b, eff)
             picks = {}
-            for variant, (tg, tc) in (("roofline", (est_g, est_c)), ("measured", (T_g, T_c))):
-                chosen, preds = c3.c3_predict_partition(tables[("gemm", gcls)], tables[("comm", kind)],
-                                                        tg, tc, per, opts)
+            for variant in variants:
+                tg, tc = (T_g, T_c) if variant[0] == "measured" else (est_g, est_c)
+                if variant[1] == "paired":
+                    gt, ct = tables[("gemm", gcls, kind)], tables[("comm", kind, gcls)]
+                else:
+                    gt, ct = tables[("gemm", gcls)], tables[("comm", kind)]
+                chosen, preds = c3.c3_predict_partition(gt, ct, tg, tc, per, opts)
                 hit = chosen == best_c
                 loss = measured[chosen] / measured[best_c] - 1.0
                 hits[variant] += hit
                 losses[variant].append(loss)
-                picks[variant] = {"chosen_cus_per_xcc": chosen, "hit": hit, "loss": round(loss, 5),
-                                  "predicted_ms": [round(p * 1e3, 4) for p in preds]}
+                picks[f"{variant[0]}_times_{variant[1]}_table"] = {
+                    "chosen_cus_per_xcc": chosen, "hit": hit, "loss": round(loss, 5),
+                    "predicted_ms": [round(p * 1e3, 4) for p in preds]}
             T_sp = m["shared"]
             mt = c3.c3_derive_metrics(T_g, T_c, measured[best_c])
             gain_rp_over_sp.append(T_sp / measured[best_c])
@@ -850,10 +887,10 @@ def run_partition(args, c3, info):
         del g
     print(json.dumps({
         "mode": "partition", "summary": True, "scenarios": n, "rounds": reps,
-        "heuristic_roofline_0.70": {"hits": hits["roofline"], "max_loss": round(max(losses["roofline"]), 5),
-                                    "mean_loss": round(statistics.mean(losses["roofline"]), 5)},
-        "heuristic_measured_times": {"hits": hits["measured"], "max_loss": round(max(losses["measured"]), 5),
-                                     "mean_loss": round(statistics.mean(losses["measured"]), 5)},
+        "heuristic": {f"{'roofline_0.70' if v[0] == 'roofline' else 'measured'}_times_{v[1]}_table":
+                      {"hits": hits[v], "within_1.5pct": sum(x <= 0.015 for x in losses[v]),
+                       "max_loss": round(max(losses[v]), 5),
+                       "mean_loss": round(statistics.mean(losses[v]), 5)} for v in variants},
         "best_split_vs_shared_cus_geomean": round(statistics.geometric_mean(gain_rp_over_sp), 4),
         "scenarios_where_best_split_beats_shared": sum(x > 1.0 for x in gain_rp_over_sp)}), flush=True)
 
