@@ -34,6 +34,8 @@ Other modes print one JSON line per measured cell:
                    scored against it
   --mode hybrid    the hybrid mover's concurrent time against its engine share on 8 workloads,
                    and the share c3_hybrid_share picks scored against the best of the sweep
+  --mode ksteps    the tile GEMM at 8192 x 28672 x K for K = 1024 ... 16384 (per-tile start/end
+                   cost against per-K-step cost)
   --mode gemm_vs_vendor  the library's GEMM against torch.matmul (hipBLASLt) on the same
                    operands, alternating single launches and back-to-back batches (a reference
                    point for kernel quality; torch's result is not used for anything else)
@@ -91,7 +93,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--mode", default="c3",
                    choices=["c3", "movers", "grid", "cus", "partition", "gemm_vs_vendor",
-                            "hybrid"])
+                            "hybrid", "ksteps"])
     p.add_argument("--workload", type=int, default=4,
                    help="workload id (1..6); 4 = the 405B-class GEMM beside the 512 MiB all-to-all")
     p.add_argument("--gather-mib", type=int, default=0, help="workload 5: total gather MiB")
@@ -895,6 +897,56 @@ def run_partition(args, c3, info):
         "scenarios_where_best_split_beats_shared": sum(x > 1.0 for x in gain_rp_over_sp)}), flush=True)
 
 
+def run_ksteps(args, c3, info):
+    """The tile GEMM against K at a fixed M x N (8192 x 28672: 14 tiles of 256 x 256 per CU), so
+    that a fit of time (or, under counters, cycles) against K steps separates the cost of a tile's
+    start and end from the cost of one K step. Every launch comes after a 512 MiB read flush; the
+    K values run in an order shuffled per round (printed, for labelling counter dispatches); C is
+    checked bit-identical across rounds."""
+    import numpy as np
+    import torch
+
+    from concurrent_gemm_dma_amd import workloads as wl
+
+    M, N = 8192, 28672
+    Ks = (1024, 2048, 4096, 8192, 16384)
+    dev = torch.device("cuda:0")
+    A = wl.gen_bf16((M, max(Ks)), ("normal", 0.0, 1.0), wl.seed_for(2, wl.BUF_A))
+    dA = torch.from_numpy(A.view(np.int16)).to(dev)
+    del A
+    B = wl.gen_bf16((max(Ks), N), ("normal", 0.0, 0.02), wl.seed_for(2, wl.BUF_B))
+    dB = torch.from_numpy(B.view(np.int16)).to(dev)
+    del B
+    ops = {K: (dA[:, :K].contiguous(), dB[:K], torch.empty((M, N), dtype=torch.int16, device=dev))
+           for K in Ks}
+    o = c3.conc_opts(flush_bytes=FLUSH_BYTES)
+    times = {K: [] for K in Ks}
+    first = {}
+    reps = max(3, args.steps)
+    for i in range(reps + 1):
+        order = list(Ks)
+        random.Random(i).shuffle(order)
+        print(json.dumps({"mode": "ksteps", "round": i, "order": order}), flush=True)
+        for K in order:
+            a, b, c = ops[K]
+            c.fill_(-1)
+            torch.cuda.synchronize()
+            t = c3.c3_run_concurrent(c3.gemm_args(a, b, c, M, N, K), None, o)
+            if not args.profile:
+                if K not in first:
+                    first[K] = c.clone()
+                elif not torch.equal(first[K], c):
+                    raise SystemExit(f"ksteps: C of K={K} differs between rounds")
+            if i:
+                times[K].append(t["gemm_gpu_ms"])
+    for K in Ks:
+        ms = statistics.median(times[K])
+        print(json.dumps({"mode": "ksteps", "M": M, "N": N, "K": K, "k_steps_per_tile": K // 32,
+                          "tiles_per_cu": M * N // (256 * 256) // info["n_cu"],
+                          "gemm_ms": round(ms, 4),
+                          "tflops": round(2.0 * M * N * K / ms / 1e9, 1)}), flush=True)
+
+
 def run_gemm_vs_vendor(args, c3, info):
     """The library's GEMM and torch.matmul (hipBLASLt) on the same bf16 operands: alternating
     event-timed single launches (median), then two batches of 20 back-to-back launches each.
@@ -1038,7 +1090,8 @@ def main():
     info = c3.c3_device_info()
     log("device:", info)
     {"c3": run_c3, "movers": run_movers, "grid": run_grid, "cus": run_cus, "hybrid": run_hybrid,
-     "partition": run_partition, "gemm_vs_vendor": run_gemm_vs_vendor}[args.mode](args, c3, info)
+     "partition": run_partition, "gemm_vs_vendor": run_gemm_vs_vendor,
+     "ksteps": run_ksteps}[args.mode](args, c3, info)
     c3.c3_finalize()
 
 
