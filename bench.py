@@ -734,7 +734,8 @@ def run_partition(args, c3, info):
 
     per = info["n_cu"] // info["n_xcc"]
     opts = [c for c in (1, 2, 4, 8, 16) if c < per]
-    reps = max(5, args.steps)
+    # at least the paper's nine measured runs per configuration (the default --steps gives 20)
+    reps = max(9, args.steps)
     eff = 0.70
     base = wl.WORKLOADS[2]
     peak_f, peak_b = PEAK_BF16_TFLOPS * 1e12, PEAK_HBM_GBPS * 1e9
