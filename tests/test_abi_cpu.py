@@ -50,6 +50,8 @@ def test_calls_before_init_are_rejected(c3):
     # require_init fails before any HIP call is made
     assert c3.call("c3_gemm", None, None, None, 1, 8, 8, None) == c3.C3_E_NOT_INIT
     assert "c3_init" in c3.c3_last_error()
+    assert c3.call("c3_gemm_noalloc", None, None, None, 1, 8, 8, None) == c3.C3_E_NOT_INIT
+    assert "c3_init" in c3.c3_last_error()
     info = c3.c3_info()
     assert c3.call("c3_device_info", info) == c3.C3_E_NOT_INIT
 
