@@ -664,7 +664,7 @@ def run_grid(args, c3, info):
             Tc = statistics.median(r[("copy", mname)] for r in rounds) * 1e-9
             for keep in keeps:
                 for cf in (False, True):
-                    Tconc = statistics.mean(r[("conc", mname, keep, cf)] for r in rounds) * 1e-9
+                    Tconc = statistics.median(r[("conc", mname, keep, cf)] for r in rounds) * 1e-9
                     m = c3.c3_derive_metrics(Tg, Tc, Tconc, float(w.gemm_bytes + 2 * copy_bytes),
                                              PEAK_HBM_GBPS * 1e9)
                     print(json.dumps({
