@@ -315,6 +315,49 @@ def cpu_baseline_and_parity(args, s, w, oracle_seconds):
     return cpu, parity
 
 
+def mover_cell(c3, t_gemm, r, *, comm_bytes, flops, hbm_total, best_copy):
+    """One mover's cell of the c3 mode from its timed rounds. t_gemm: the isolated GEMM's host
+    times (s), one per round; r: the mover's per-round lists "t_copy", "t_conc" (host, s),
+    "c_gpu" (the copy's GPU time, s), "gk" (the GEMM kernel's event time in the concurrent run,
+    s) and "done" ((GEMM, copy) completion seen by the library, ms from the first issue).
+    The speedup metrics take the median of each of the three times; the dispersion is the
+    quartiles of the uplift computed from each round's own three times."""
+    T_gemm = statistics.median(t_gemm)
+    T_copy = statistics.median(r["t_copy"])
+    T_conc_med = statistics.median(r["t_conc"])
+    T_conc_mean = statistics.mean(r["t_conc"])
+    c_gpu_med = statistics.median(r["c_gpu"])
+    m = c3.c3_derive_metrics(T_gemm, T_copy, T_conc_med, hbm_total, PEAK_HBM_GBPS * 1e9)
+    per_round = sorted(c3.c3_derive_metrics(tg, tc, tx, hbm_total, PEAK_HBM_GBPS * 1e9)
+                       ["uplift_fraction"] for tg, tc, tx in zip(t_gemm, r["t_copy"], r["t_conc"]))
+    copy_done_s = statistics.median(d[1] for d in r["done"]) * 1e-3
+    return {
+        "t_copy_ms": T_copy * 1e3, "t_conc_ms": T_conc_med * 1e3,
+        "t_conc_ms_mean": T_conc_mean * 1e3,
+        "t_conc_ms_min": min(r["t_conc"]) * 1e3, "t_conc_ms_max": max(r["t_conc"]) * 1e3,
+        "t_conc_ms_std": (statistics.pstdev(r["t_conc"]) * 1e3) if len(r["t_conc"]) > 1 else 0.0,
+        "copy_gbps_isolated": comm_bytes / T_copy / 1e9,
+        "copy_gbps_isolated_engine_clock": (comm_bytes / c_gpu_med / 1e9 if c_gpu_med > 0 else None),
+        "gemm_tflops_concurrent": flops / T_conc_mean / 1e12,
+        # the copy's own rate beside the GEMM: its bytes over the time from the first issue to the
+        # copy's observed completion (not over the whole concurrent run)
+        "copy_gbps_concurrent": comm_bytes / copy_done_s / 1e9 if copy_done_s > 0 else None,
+        "uplift_per_round_p25_median_p75": [per_round[len(per_round) // 4],
+                                            statistics.median(per_round),
+                                            per_round[(3 * len(per_round)) // 4]],
+        "gemm_kernel_ms_concurrent": statistics.mean(r["gk"]) * 1e3,
+        # overlap evidence on the library's clock: when each operation was seen complete
+        "gemm_done_ms_median": statistics.median(d[0] for d in r["done"]),
+        "copy_done_ms_median": statistics.median(d[1] for d in r["done"]),
+        "speedup_vs_best_serial": (T_gemm + best_copy) / T_conc_med,
+        **{k: m[k] for k in ("ideal_speedup", "speedup", "uplift_fraction", "ratio_of_ideal",
+                             "gemm_slowdown", "hbm_ceiling", "taxonomy")},
+        # overlap cannot beat running both at their isolated speeds: a realized speedup above the
+        # ideal means the isolated times were measured slow (a measurement anomaly)
+        "anomaly_speedup_above_ideal": bool(m["speedup"] > m["ideal_speedup"] * 1.001),
+    }
+
+
 def run_c3(args, c3, info):
     from concurrent_gemm_dma_amd import workloads as wl
 
@@ -425,58 +468,26 @@ def run_c3(args, c3, info):
     results = {}
     # the faster of the paper's two movers: a cell cannot look good against its own slow serial time
     best_copy = min(statistics.median(rec[name]["t_copy"]) for name in ("sdma", "cu"))
-    hbm_total = float(w.gemm_bytes + comm_bytes)
     for name, _ in movers:
         r = rec[name]
-        # the derived metrics take the median of each of the three times (one statistic for all)
-        T_copy = statistics.median(r["t_copy"])
-        T_conc_med = statistics.median(r["t_conc"])
-        T_conc_mean = statistics.mean(r["t_conc"])
-        c_gpu_med = statistics.median(r["c_gpu"])
-        m = c3.c3_derive_metrics(T_gemm, T_copy, T_conc_med, hbm_total, PEAK_HBM_GBPS * 1e9)
-        # dispersion: the uplift of every timed round from that round's own three times
-        per_round = sorted(c3.c3_derive_metrics(tg, tc, tx, hbm_total, PEAK_HBM_GBPS * 1e9)
-                           ["uplift_fraction"] for tg, tc, tx in zip(t_gemm, r["t_copy"], r["t_conc"]))
-        copy_done_s = statistics.median(d[1] for d in r["done"]) * 1e-3
-        results[name] = {
-            "t_copy_ms": T_copy * 1e3, "t_conc_ms": T_conc_med * 1e3,
-            "t_conc_ms_mean": T_conc_mean * 1e3,
-            "t_conc_ms_min": min(r["t_conc"]) * 1e3, "t_conc_ms_max": max(r["t_conc"]) * 1e3,
-            "t_conc_ms_std": (statistics.pstdev(r["t_conc"]) * 1e3) if len(r["t_conc"]) > 1 else 0.0,
-            "copy_gbps_isolated": comm_bytes / T_copy / 1e9,
-            "copy_gbps_isolated_engine_clock": (comm_bytes / c_gpu_med / 1e9
-                                                if c_gpu_med > 0 else None),
-            "gemm_tflops_concurrent": flops / T_conc_mean / 1e12,
-            # the copy's own rate beside the GEMM: its bytes over the time from the first issue
-            # to the copy's observed completion (not over the whole concurrent run)
-            "copy_gbps_concurrent": comm_bytes / copy_done_s / 1e9 if copy_done_s > 0 else None,
-            "uplift_per_round_p25_median_p75": [per_round[len(per_round) // 4],
-                                                statistics.median(per_round),
-                                                per_round[(3 * len(per_round)) // 4]],
-            "gemm_kernel_ms_concurrent": statistics.mean(r["gk"]) * 1e3,
-            # overlap evidence on the library's clock: when each operation was seen complete
-            "gemm_done_ms_median": statistics.median(d[0] for d in r["done"]),
-            "copy_done_ms_median": statistics.median(d[1] for d in r["done"]),
-            **({"sdma_permille": hybrid_pm} if name == "hybrid" else {}),
-            "speedup_vs_best_serial": (T_gemm + best_copy) / T_conc_med,
-            **({"reduce_scatter_ms_isolated": statistics.median(r["rs"]) * 1e3,
-                "reduce_scatter_gbps_isolated": ((w.units + 1) * w.unit_bytes
-                                                 / statistics.median(r["rs"]) / 1e9)}
-               if w.copy == "allreduce" else {}),
-            **{k: m[k] for k in ("ideal_speedup", "speedup", "uplift_fraction", "ratio_of_ideal",
-                                 "gemm_slowdown", "hbm_ceiling", "taxonomy")},
-            # overlap cannot beat running both at their isolated speeds: a realized speedup above
-            # the ideal means the isolated times were measured slow (a measurement anomaly)
-            "anomaly_speedup_above_ideal": bool(m["speedup"] > m["ideal_speedup"] * 1.001),
-        }
-        if results[name]["anomaly_speedup_above_ideal"]:
-            log(f"{name}: WARNING realized speedup {m['speedup']:.4f} above the ideal "
-                f"{m['ideal_speedup']:.4f}: isolated timings suspect")
-        log(f"{name}: T_copy {T_copy * 1e3:.3f} ms ({results[name]['copy_gbps_isolated']:.0f} GB/s), "
-            f"T_conc median {T_conc_med * 1e3:.3f} ms (mean {T_conc_mean * 1e3:.3f}), "
-            f"S {m['speedup']:.4f} / ideal {m['ideal_speedup']:.4f}, "
-            f"uplift {m['uplift_fraction'] * 100:.1f}% (per-round quartiles "
-            f"{per_round[len(per_round) // 4] * 100:.1f}..{per_round[(3 * len(per_round)) // 4] * 100:.1f}%)")
+        res = mover_cell(c3, t_gemm, r, comm_bytes=comm_bytes, flops=flops,
+                         hbm_total=float(w.gemm_bytes + comm_bytes), best_copy=best_copy)
+        if name == "hybrid":
+            res["sdma_permille"] = hybrid_pm
+        if w.copy == "allreduce":
+            res["reduce_scatter_ms_isolated"] = statistics.median(r["rs"]) * 1e3
+            res["reduce_scatter_gbps_isolated"] = ((w.units + 1) * w.unit_bytes
+                                                   / statistics.median(r["rs"]) / 1e9)
+        results[name] = res
+        if res["anomaly_speedup_above_ideal"]:
+            log(f"{name}: WARNING realized speedup {res['speedup']:.4f} above the ideal "
+                f"{res['ideal_speedup']:.4f}: isolated timings suspect")
+        q = res["uplift_per_round_p25_median_p75"]
+        log(f"{name}: T_copy {res['t_copy_ms']:.3f} ms ({res['copy_gbps_isolated']:.0f} GB/s), "
+            f"T_conc median {res['t_conc_ms']:.3f} ms (mean {res['t_conc_ms_mean']:.3f}), "
+            f"S {res['speedup']:.4f} / ideal {res['ideal_speedup']:.4f}, "
+            f"uplift {res['uplift_fraction'] * 100:.1f}% (per-round quartiles "
+            f"{q[0] * 100:.1f}..{q[2] * 100:.1f}%)")
 
     # ---- roofline of the dominant kernel (the GEMM): HIP events recorded by the library on the
     # GEMM's own stream around every launch of the timed SDMA-concurrent steps ----
