@@ -36,6 +36,8 @@ Other modes print one JSON line per measured cell:
                    and the share c3_hybrid_share picks scored against the best of the sweep
   --mode ksteps    the tile GEMM at 8192 x 28672 x K for K = 1024 ... 16384 (per-tile start/end
                    cost against per-K-step cost)
+  --mode mfma_ceiling  the matrix cores' sustained bf16 rate with nothing but MFMAs in flight
+                   (the power-limited ceiling for any GEMM kernel on this chip)
   --mode gemm_vs_vendor  the library's GEMM against torch.matmul (hipBLASLt) on the same
                    operands, alternating single launches and back-to-back batches (a reference
                    point for kernel quality; torch's result is not used for anything else)
@@ -93,7 +95,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--mode", default="c3",
                    choices=["c3", "movers", "grid", "cus", "partition", "gemm_vs_vendor",
-                            "hybrid", "ksteps"])
+                            "hybrid", "ksteps", "mfma_ceiling"])
     p.add_argument("--workload", type=int, default=4,
                    help="workload id (1..6); 4 = the 405B-class GEMM beside the 512 MiB all-to-all")
     p.add_argument("--gather-mib", type=int, default=0, help="workload 5: total gather MiB")
@@ -959,6 +961,40 @@ def run_ksteps(args, c3, info):
                           "tflops": round(2.0 * M * N * K / ms / 1e9, 1)}), flush=True)
 
 
+def run_mfma_ceiling(args, c3, info):
+    """The matrix cores' sustained bf16 rate with nothing but MFMAs in flight (c3_probe_mfma_rate:
+    one workgroup of 4 waves per CU, each wave 16 independent 32x32 accumulators), for runs as
+    long as the workload-2 and workload-4 GEMMs, each after a 512 MiB read flush, timed with HIP
+    events on the probe's stream. The ceiling for any bf16 GEMM on this chip at its power limit."""
+    import torch
+
+    n_wg = info["n_cu"]
+    s = torch.cuda.Stream()
+    out = torch.empty(n_wg * 256, dtype=torch.float64, device="cuda:0")
+    reps = max(3, args.steps)
+    # random operands (bits toggling as a GEMM's data do) and small-integer ones, for runs about
+    # as long as the workload-2 and workload-4 GEMMs
+    for random, iters in ((1, 8400), (1, 33600), (0, 8400), (0, 33600)):
+        flops = float(n_wg) * 4 * iters * 16 * 32768
+        ms = []
+        for i in range(reps + 1):
+            torch.cuda.synchronize()
+            c3.c3_flush_llc(FLUSH_BYTES, s)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            c3.c3_probe_mfma_rate(out, n_wg, iters, random, s)
+            e1.record(s)
+            torch.cuda.synchronize()
+            if i:
+                ms.append(e0.elapsed_time(e1))
+        m = statistics.median(ms)
+        print(json.dumps({"mode": "mfma_ceiling", "operands": "random" if random else "small integers",
+                          "workgroups": n_wg, "iterations": iters,
+                          "ms": round(m, 4), "tflops": round(flops / m / 1e9, 1),
+                          "frac_of_peak": round(flops / m / 1e9 / PEAK_BF16_TFLOPS, 4),
+                          "ms_min": round(min(ms), 4), "ms_max": round(max(ms), 4)}), flush=True)
+
+
 def run_gemm_vs_vendor(args, c3, info):
     """The library's GEMM and torch.matmul (hipBLASLt) on the same bf16 operands: alternating
     event-timed single launches (median), then two batches of 20 back-to-back launches each.
@@ -1103,7 +1139,7 @@ def main():
     log("device:", info)
     {"c3": run_c3, "movers": run_movers, "grid": run_grid, "cus": run_cus, "hybrid": run_hybrid,
      "partition": run_partition, "gemm_vs_vendor": run_gemm_vs_vendor,
-     "ksteps": run_ksteps}[args.mode](args, c3, info)
+     "ksteps": run_ksteps, "mfma_ceiling": run_mfma_ceiling}[args.mode](args, c3, info)
     c3.c3_finalize()
 
 

@@ -40,13 +40,13 @@ C3_MAX_MASK_WORDS = 8
 C3_MAX_WORLD = 64
 C3_MAX_CURVE = 16
 C3_NOALLOC_SCRATCH_BYTES = 16 << 20  # c3_gemm_noalloc: fixed split-K partials per device
-C3_ABI_VERSION = 4
+C3_ABI_VERSION = 5
 TAXONOMY = {0: "GC-equal", 1: "G-long", 2: "C-long"}
 
 # Every symbol include/c3.h declares.
 EXPORTS = ("c3_init", "c3_finalize", "c3_last_error", "c3_device_info", "c3_stream_create",
            "c3_stream_destroy", "c3_cu_mask_balanced", "c3_probe_placement", "c3_gemm",
-           "c3_gemm_noalloc",
+           "c3_gemm_noalloc", "c3_probe_mfma_rate",
            "c3_gather", "c3_all2all_block", "c3_reduce_scatter", "c3_allreduce_local",
            "c3_flush_llc", "c3_run_concurrent", "c3_derive_metrics", "c3_roofline_time",
            "c3_predict_partition", "c3_hybrid_share")
@@ -168,6 +168,7 @@ def load(path: Optional[str] = None):
     L.c3_stream_destroy.argtypes = [vp]
     L.c3_cu_mask_balanced.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_uint32)]
     L.c3_probe_placement.argtypes = [vp, ctypes.c_int, vp]
+    L.c3_probe_mfma_rate.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     L.c3_gemm.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp]
     L.c3_gemm_noalloc.argtypes = [vp, vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp]
     L.c3_gather.argtypes = [vp, ctypes.POINTER(vp), ctypes.c_int, ctypes.c_size_t, ctypes.c_int,
@@ -272,6 +273,12 @@ def c3_cu_mask_balanced(keep_per_xcc: int, complement: bool = False) -> list:
 
 def c3_probe_placement(out_dev, n_blocks: int, stream=None) -> None:
     check(load().c3_probe_placement(_stream(stream), n_blocks, _ptr(out_dev)))
+
+
+def c3_probe_mfma_rate(out_dev, n_workgroups: int, iterations: int, random: int = 1,
+                       stream=None) -> None:
+    check(load().c3_probe_mfma_rate(_stream(stream), n_workgroups, iterations, random,
+                                    _ptr(out_dev)))
 
 
 def c3_gemm(A, B, C, M: int, N: int, K: int, stream=None) -> None:

@@ -267,6 +267,21 @@ c3_status c3_probe_placement(void* stream, int n_blocks, uint32_t* out_dev) {
     })
 }
 
+c3_status c3_probe_mfma_rate(void* stream, int n_workgroups, int iterations, int random,
+                             double* out_dev) {
+    C3_ENTRY({
+        C3_TRY(require_init());
+        if (n_workgroups < 1 || n_workgroups > 65536)
+            return fail(C3_E_INVALID, "n_workgroups must be in [1, 65536]");
+        if (iterations < 1 || iterations > 262144)
+            return fail(C3_E_INVALID, "iterations must be in [1, 262144]");
+        C3_TRY(check_device_ptr(out_dev, (size_t)n_workgroups * 256 * sizeof(double), "probe out"));
+        if (random != 0 && random != 1) return fail(C3_E_INVALID, "random must be 0 or 1");
+        return mfma_probe_enqueue(n_workgroups, iterations, random, out_dev,
+                                  static_cast<hipStream_t>(stream));
+    })
+}
+
 c3_status c3_gemm(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                   void* stream) {
     C3_ENTRY({

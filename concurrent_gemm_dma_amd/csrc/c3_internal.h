@@ -98,6 +98,10 @@ c3_status copy_cu_enqueue(const std::vector<Segment>& segs, const c3_move_opts& 
 c3_status flush_enqueue(void* buf, size_t bytes, hipStream_t stream);
 c3_status probe_enqueue(int n_blocks, uint32_t* out_dev, hipStream_t stream);
 
+// ---- MFMA rate probe (probe.hip) ---------------------------------------------------------------
+c3_status mfma_probe_enqueue(int n_workgroups, int iters, int random, double* out_dev,
+                             hipStream_t stream);
+
 // ---- reduce-scatter (reduce.hip) ------------------------------------------------------------------
 constexpr int kMaxWorld = C3_MAX_WORLD;
 struct ReduceArgs {

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define C3_ABI_VERSION 4
+#define C3_ABI_VERSION 5
 #define C3_MAX_MASK_WORDS 8 /* CU masks cover up to 256 CUs, bit i = CU i as the driver numbers it */
 #define C3_MAX_SEGMENTS 4096
 #define C3_MAX_WORLD 64 /* ranks of a reduce-scatter / all-reduce local share */
@@ -253,6 +253,22 @@ c3_status c3_cu_mask_balanced(int keep_per_xcc, int complement, uint32_t* mask_o
 /* Record where `n_blocks` one-wave workgroups ran: out_dev (device, 2*n_blocks uint32) gets the
  * raw HW_ID and XCC_ID registers of each workgroup. Synchronous. Used to verify CU masks. */
 c3_status c3_probe_placement(void* stream, int n_blocks, uint32_t* out_dev);
+
+/* Measurement probe: the matrix cores' sustained bf16 rate on this device with nothing but MFMAs
+ * in flight, the ceiling for any bf16 GEMM here (under sustained MFMA load the chip runs at the
+ * clock its power limit allows, and the power an MFMA draws depends on how many operand bits
+ * toggle). n_workgroups workgroups of 4 waves; each wave keeps 16 independent 32x32 fp32
+ * accumulators and issues `iterations` rounds of 16 v_mfma_f32_32x32x16_bf16, i.e.
+ * n_workgroups * 4 * iterations * 16 * 32768 FLOP, on two operand sets used alternately:
+ * random = 0: small integers (-2..2), every sum exact; random = 1: random signs, exponents and
+ * mantissas, as a GEMM's data. out_dev (device, n_workgroups * 256 doubles) gets each lane's sum
+ * of its accumulators; a wave's 64 sums total iterations * 8 * (S0 + S1) (exactly for random = 0,
+ * up to fp32 rounding for random = 1; the operand formulas are in probe.hip). Stream-ordered and
+ * asynchronous (time it with events on `stream`). 1 <= n_workgroups <= 65536,
+ * 1 <= iterations <= 262144 (the largest count whose integer sums stay exact in fp32),
+ * random in {0, 1}, else C3_E_INVALID. */
+c3_status c3_probe_mfma_rate(void* stream, int n_workgroups, int iterations, int random,
+                             double* out_dev);
 
 /* ---------------------------------------------------------------------------------------------
  * The two operations (isolated)
