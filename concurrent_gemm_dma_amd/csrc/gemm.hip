@@ -8,8 +8,8 @@
 //   4x4 v_mfma_f32_32x32x16_bf16. Operands go global -> LDS directly (LDS-direct buffer loads),
 //   K step 32: A in slabs of 64 k (full 128-byte lines), three in LDS, B in four 32-k stages.
 //   The MFMA is fed transposed (B^T as the row operand, A^T as the
-//   column operand), so each lane's accumulators are 4 consecutive columns of one C row and the
-//   epilogue writes 8-byte runs. B stays K x N in LDS and is read with the LDS transpose load
+//   column operand), so each lane's accumulators are 4 consecutive columns of one C row; the
+//   epilogue regroups them through LDS into 16-byte runs along C's rows. B stays K x N in LDS and is read with the LDS transpose load
 //   (ds_read_b64_tr_b16), which hands each lane 4 consecutive k of one column. With fewer tiles
 //   than CUs, K can also be split over a second grid dimension (fp32 partials, summed in split
 //   order by splitk_reduce). Shapes with M > 64 use this kernel unless the 128 kernel wins.
@@ -504,25 +504,44 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     // ---- epilogue: lane holds C[m][n..n+3], m = mi*32 + lane%32, n = ni*32 + 8g + 4*(lane/32);
     // one K split writes bf16 C, several write fp32 partials ws[y][m][n] for splitk_reduce
     if (!SPLIT) {
-        const __amdgpu_buffer_rsrc_t rC =
-            make_rsrc(C + (size_t)m0 * N + n0, ((int64_t)(M - m0) * N - n0) * 2);
+        // Stored straight from the accumulator layout, each store instruction would write 16
+        // bytes into each of 32 rows, and the 64 such stores per wave hold the CU's vector memory
+        // path for about 15 000 cycles per tile. So each wave stages its 128 x 128 bf16 sub-tile in
+        // LDS (free once every wave has read its last fragments; 32 KiB per wave, rows of 256 B,
+        // 16-byte chunk ^= row & 15, so that the 8-byte writes of 32 rows and the 16-byte reads
+        // along 4 rows each spread over all banks) and stores it back as 16 bytes per lane along
+        // the rows: four 256-byte row pieces per instruction, 32 instructions per wave.
+        // N is a multiple of 8, so a 16-byte chunk lies wholly inside or wholly outside N.
+        __syncthreads();
+        C3_LDS char* stg = (C3_LDS char*)smem + wave * (BM / 2) * (BN / 2) * 2;
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-            const int ml = wm * 128 + mi * 32 + (lane & 31);
-            const bool mvalid = (m0 + ml) < M;
+            const int r = mi * 32 + (lane & 31);
 #pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
+            for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int nl = wn * 128 + ni * 32 + 8 * g + 4 * (lane >> 5);
-                    const bool ok = mvalid && (n0 + nl) < N;
-                    const uint32_t off =
-                        ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 2u : kOOB;
+                    const int chunk = ni * 4 + g;
+                    const uint32_t off = (uint32_t)r * 256u + (uint32_t)((chunk ^ (r & 15)) << 4) +
+                                         8u * (uint32_t)(lane >> 5);
                     const f32x16_t& a = acc[mi][ni];
-                    store8(rC, off,
-                           pack_bf16x4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]));
+                    *reinterpret_cast<C3_LDS u32x2_t*>(stg + off) =
+                        pack_bf16x4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
                 }
-            }
+        }
+        const __amdgpu_buffer_rsrc_t rC =
+            make_rsrc(C + (size_t)m0 * N + n0, ((int64_t)(M - m0) * N - n0) * 2);
+        const int chunk = lane & 15;
+        const int nl = wn * 128 + chunk * 8;
+        const bool nvalid = (n0 + nl) < N;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int r = i * 4 + (lane >> 4);
+            const u32x4_t v = *reinterpret_cast<const C3_LDS u32x4_t*>(
+                stg + (uint32_t)r * 256u + (uint32_t)((chunk ^ (r & 15)) << 4));
+            const int ml = wm * 128 + r;
+            const bool ok = nvalid && (m0 + ml) < M;
+            store16(rC, ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 2u : kOOB, v);
         }
     } else {
         float* wsb = ws + ((size_t)blockIdx.y * M + m0) * N + n0;
