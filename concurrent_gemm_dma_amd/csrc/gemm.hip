@@ -473,26 +473,43 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
     for (int j = 0; j < 12; ++j) read_item(0, 0, 0, j);
     int kt = 0;
     const int nkf = Ke / BK;
-    if (kt + 18 <= nkf) {
-        const uint64_t b0 = (uint64_t)(uintptr_t)(B + (size_t)(kt + NSTAGE - 1) * BK * N + n0);
+    {
+        const uint64_t b0 = (uint64_t)(uintptr_t)(B + (size_t)(NSTAGE - 1) * BK * N + n0);
         fb_lo = (uint32_t)b0;
         fb_hi = (uint32_t)(b0 >> 32);
         fa0 = 0u;
-        for (; kt + 18 <= nkf; kt += 12) {
-            step_fast(std::integral_constant<int, 0>{});
-            step_fast(std::integral_constant<int, 1>{});
-            step_fast(std::integral_constant<int, 2>{});
-            step_fast(std::integral_constant<int, 3>{});
-            step_fast(std::integral_constant<int, 4>{});
-            step_fast(std::integral_constant<int, 5>{});
-            step_fast(std::integral_constant<int, 6>{});
-            step_fast(std::integral_constant<int, 7>{});
-            step_fast(std::integral_constant<int, 8>{});
-            step_fast(std::integral_constant<int, 9>{});
-            step_fast(std::integral_constant<int, 10>{});
-            step_fast(std::integral_constant<int, 11>{});
-        }
     }
+    for (; kt + 18 <= nkf; kt += 12) {
+        step_fast(std::integral_constant<int, 0>{});
+        step_fast(std::integral_constant<int, 1>{});
+        step_fast(std::integral_constant<int, 2>{});
+        step_fast(std::integral_constant<int, 3>{});
+        step_fast(std::integral_constant<int, 4>{});
+        step_fast(std::integral_constant<int, 5>{});
+        step_fast(std::integral_constant<int, 6>{});
+        step_fast(std::integral_constant<int, 7>{});
+        step_fast(std::integral_constant<int, 8>{});
+        step_fast(std::integral_constant<int, 9>{});
+        step_fast(std::integral_constant<int, 10>{});
+        step_fast(std::integral_constant<int, 11>{});
+    }
+    // Past the last whole group (kt % 12 == 0 here), fast steps go on, in the group's phase, for
+    // as long as the loads a step issues lie wholly inside K: B of step kt+3 and the slab
+    // (kt+5)/2. The test only turns false as kt grows and kt moves only when a step runs, so
+    // once one test fails every later one fails too.
+    auto fast_ok = [&](int k) { return k + NSTAGE <= nkf && 64 * ((k + 5) >> 1) + 64 <= Ke; };
+    if (fast_ok(kt)) { step_fast(std::integral_constant<int, 0>{}); ++kt; }
+    if (fast_ok(kt)) { step_fast(std::integral_constant<int, 1>{}); ++kt; }
+    if (fast_ok(kt)) { step_fast(std::integral_constant<int, 2>{}); ++kt; }
+    if (fast_ok(kt)) { step_fast(std::integral_constant<int, 3>{}); ++kt; }
+    if (fast_ok(kt)) { step_fast(std::integral_constant<int, 4>{}); ++kt; }
+    if (fast_ok(kt)) { step_fast(std::integral_constant<int, 5>{}); ++kt; }
+    if (fast_ok(kt)) { step_fast(std::integral_constant<int, 6>{}); ++kt; }
+    if (fast_ok(kt)) { step_fast(std::integral_constant<int, 7>{}); ++kt; }
+    if (fast_ok(kt)) { step_fast(std::integral_constant<int, 8>{}); ++kt; }
+    if (fast_ok(kt)) { step_fast(std::integral_constant<int, 9>{}); ++kt; }
+    if (fast_ok(kt)) { step_fast(std::integral_constant<int, 10>{}); ++kt; }
+    if (fast_ok(kt)) { step_fast(std::integral_constant<int, 11>{}); ++kt; }
     for (; kt + NSTAGE < nk; ++kt) step(kt, T{}, T{}, T{});
     if (kt + NSTAGE - 1 < nk) {
         step(kt, T{}, F{}, T{});
