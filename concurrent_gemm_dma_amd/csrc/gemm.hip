@@ -524,10 +524,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         // Stored straight from the accumulator layout, each store instruction would write 16
         // bytes into each of 32 rows, and the 64 such stores per wave hold the CU's vector memory
         // path for about 15 000 cycles per tile. So each wave stages its 128 x 128 bf16 sub-tile in
-        // LDS (free once every wave has read its last fragments; 32 KiB per wave, rows of 256 B,
-        // 16-byte chunk ^= row & 15, so that the 8-byte writes of 32 rows and the 16-byte reads
-        // along 4 rows each spread over all banks) and stores it back as 16 bytes per lane along
-        // the rows: four 256-byte row pieces per instruction, 32 instructions per wave.
+        // LDS (free once every wave has read its last fragments; 32 KiB per wave, rows of 256 B)
+        // and stores it back as 16 bytes per lane along the rows: four 256-byte row pieces per
+        // instruction, 32 instructions per wave. Layout: 16-byte chunk ^= row & 15, and the two
+        // 8-byte halves of a chunk swapped in rows with bit 4 set, so that an 8-byte write by 32
+        // lanes (32 rows, one half each) and a 16-byte read by 16 lanes (one row) each touch
+        // every bank once. The four rows one read instruction covers share bit 4, so the reads
+        // undo the swap with a fixed register permutation.
         // N is a multiple of 8, so a 16-byte chunk lies wholly inside or wholly outside N.
         __syncthreads();
         C3_LDS char* stg = (C3_LDS char*)smem + wave * (BM / 2) * (BN / 2) * 2;
@@ -540,7 +543,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
                 for (int g = 0; g < 4; ++g) {
                     const int chunk = ni * 4 + g;
                     const uint32_t off = (uint32_t)r * 256u + (uint32_t)((chunk ^ (r & 15)) << 4) +
-                                         8u * (uint32_t)(lane >> 5);
+                                         8u * (uint32_t)((lane >> 5) ^ ((r >> 4) & 1));
                     const f32x16_t& a = acc[mi][ni];
                     *reinterpret_cast<C3_LDS u32x2_t*>(stg + off) =
                         pack_bf16x4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
@@ -554,8 +557,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
             const int r = i * 4 + (lane >> 4);
-            const u32x4_t v = *reinterpret_cast<const C3_LDS u32x4_t*>(
+            u32x4_t v = *reinterpret_cast<const C3_LDS u32x4_t*>(
                 stg + (uint32_t)r * 256u + (uint32_t)((chunk ^ (r & 15)) << 4));
+            if ((i >> 2) & 1) v = __builtin_shufflevector(v, v, 2, 3, 0, 1);
             const int ml = wm * 128 + r;
             const bool ok = nvalid && (m0 + ml) < M;
             store16(rC, ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 2u : kOOB, v);

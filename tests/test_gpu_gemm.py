@@ -201,6 +201,23 @@ def test_gemm_unrolled_loop_edges(c3gpu, M, N, K, splits, monkeypatch):
     check_tol(oracle.gemm_f64acc(A, B), run_gemm(c3gpu, A, B))
 
 
+@pytest.mark.parametrize("K", [32 * s for s in range(4, 30)] + [32 * s + 8 for s in (17, 18, 23, 29)]
+                         + [32 * s + 24 for s in (18, 25)])
+def test_gemm_fast_steps_past_the_last_group(c3gpu, K, monkeypatch):
+    """Past the last whole group of twelve unrolled K steps the fast steps go on while every load
+    a step issues lies inside K, then the general step takes over: every remainder after one
+    group (6..17 steps), K with no whole group at all, odd and even step counts (the last A slab
+    half or wholly used) and ragged K (a partial last step). Rows past M go through the fast
+    steps too. Bit-exact on integer-valued operands."""
+    M, N = 264, 256
+    print(f"fast-tail GEMM {M}x{N}x{K}", flush=True)
+    monkeypatch.setenv("C3_GEMM_TILE", "256")
+    monkeypatch.setenv("C3_GEMM_SPLITS", "1")
+    Ai = wl.gen_small_int_bf16((M, K), 8200 + K)
+    Bi = wl.gen_small_int_bf16((K, N), 8201 + K)
+    np.testing.assert_array_equal(run_gemm(c3gpu, Ai, Bi), oracle.gemm_f32acc(Ai, Bi))
+
+
 @pytest.mark.parametrize("M,N,K,tile,splits", [
     (300, 520, 1000, "256", "1"),   # 256 tile: partial tile rows and columns, K tail of 8
     (520, 264, 4136, "256", "2"),   # 256 tile, K split: each split's own tail
