@@ -114,9 +114,12 @@ __device__ __forceinline__ int swz_b(int krow) {
     return (r << 2) ^ (((r ^ (r >> 1)) & 1) << 1);
 }
 
-// Workgroup -> output tile. The dispatcher places workgroup b on XCD (b mod 8); renumber so that
-// each XCD gets a contiguous range of logical tiles, then walk tiles in groups of GROUP_M tile
-// rows so that the tiles resident at one time on an XCD share A rows and B columns in its L2.
+// Workgroup -> output tile. The dispatcher deals workgroups to the XCDs in turn: workgroup b runs
+// on XCD (b + s) mod 8, where the start s moves on from one dispatch to the next (measured, on
+// plain and CU-masked queues alike), so the workgroups of one residue b mod 8 share an XCD.
+// Renumber so that each residue gets a contiguous range of logical tiles, then walk tiles in
+// groups of GROUP_M tile rows so that the tiles resident at one time on an XCD share A rows and B
+// columns in its L2.
 template <int GROUP_M>
 __device__ __forceinline__ void map_tile(int bid, int nblocks, int tiles_m, int tiles_n, int& tm,
                                          int& tn) {
@@ -533,11 +536,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         // path for about 15 000 cycles per tile. So each wave stages its 128 x 128 bf16 sub-tile in
         // LDS (free once every wave has read its last fragments; 32 KiB per wave, rows of 256 B)
         // and stores it back as 16 bytes per lane along the rows: four 256-byte row pieces per
-        // instruction, 32 instructions per wave. Layout: 16-byte chunk ^= row & 15, and the two
-        // 8-byte halves of a chunk swapped in rows with bit 4 set, so that an 8-byte write by 32
-        // lanes (32 rows, one half each) and a 16-byte read by 16 lanes (one row) each touch
-        // every bank once. The four rows one read instruction covers share bit 4, so the reads
-        // undo the swap with a fixed register permutation.
+        // instruction, 32 instructions per wave. Layout: 16-byte chunk ^= (row >> 1) & 15, and
+        // the two 8-byte halves of a chunk swapped in odd rows. The LDS serves 512 bytes per
+        // cycle (128 banks of 4 bytes) when it can: a wave's 8-byte writes (32 rows, two halves
+        // each) then fill 64 distinct 8-byte slots of two rows' 512 bytes, and its 16-byte reads
+        // (four rows of 16 chunks) cover each pair of rows once; with 256 bytes (64 banks) per
+        // cycle the 32 lanes of one half-row write and the 16 lanes of one row read still touch
+        // every bank once. Reads of odd rows swap the halves back.
         // N is a multiple of 8, so a 16-byte chunk lies wholly inside or wholly outside N.
         __syncthreads();
         C3_LDS char* stg = (C3_LDS char*)smem + wave * (BM / 2) * (BN / 2) * 2;
@@ -549,8 +554,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int chunk = ni * 4 + g;
-                    const uint32_t off = (uint32_t)r * 256u + (uint32_t)((chunk ^ (r & 15)) << 4) +
-                                         8u * (uint32_t)((lane >> 5) ^ ((r >> 4) & 1));
+                    const uint32_t off = (uint32_t)r * 256u +
+                                         (uint32_t)((chunk ^ ((r >> 1) & 15)) << 4) +
+                                         8u * (uint32_t)((lane >> 5) ^ (r & 1));
                     const f32x16_t& a = acc[mi][ni];
                     *reinterpret_cast<C3_LDS u32x2_t*>(stg + off) =
                         pack_bf16x4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
@@ -565,8 +571,8 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         for (int i = 0; i < 32; ++i) {
             const int r = i * 4 + (lane >> 4);
             u32x4_t v = *reinterpret_cast<const C3_LDS u32x4_t*>(
-                stg + (uint32_t)r * 256u + (uint32_t)((chunk ^ (r & 15)) << 4));
-            if ((i >> 2) & 1) v = __builtin_shufflevector(v, v, 2, 3, 0, 1);
+                stg + (uint32_t)r * 256u + (uint32_t)((chunk ^ ((r >> 1) & 15)) << 4));
+            if (r & 1) v = __builtin_shufflevector(v, v, 2, 3, 0, 1);
             const int ml = wm * 128 + r;
             const bool ok = nvalid && (m0 + ml) < M;
             store16(rC, ok ? ((uint32_t)ml * (uint32_t)N + (uint32_t)nl) * 2u : kOOB, v);

@@ -82,6 +82,32 @@ def test_cu_mask_placement(c3gpu):
             assert not (kept[x] & comp.get(x, set())), "mask and complement share a CU"
 
 
+@pytest.mark.parametrize("keep", [None, 32, 28, 4])
+def test_workgroups_of_one_residue_share_an_xcc(c3gpu, keep):
+    """The tile GEMM groups its tiles per XCD by workgroup id mod 8 (the dispatcher deals
+    workgroups to the XCDs in turn, from a start that moves between dispatches): every workgroup
+    of one residue b mod n_xcc must land on one XCC, on a plain stream and under balanced CU
+    masks, so that the grouping holds whatever mask the GEMM runs under."""
+    info = c3gpu.c3_device_info()
+    n_xcc = info["n_xcc"]
+    per_xcc = info["n_cu"] // n_xcc
+    if keep is not None and keep > per_xcc:
+        pytest.skip(f"{keep} CUs per XCC exceed the device's {per_xcc}")
+    mask = None if keep is None else c3gpu.c3_cu_mask_balanced(keep)
+    st = c3gpu.c3_stream_create(mask)
+    try:
+        places = probe(c3gpu, st, n_blocks=2048)
+    finally:
+        sync()
+        c3gpu.c3_stream_destroy(st)
+    xcc = places[:, 0]
+    b = np.arange(len(xcc))
+    first = xcc[:n_xcc]
+    print(f"keep={keep}: first workgroups on XCCs {first.tolist()}", flush=True)
+    assert sorted(first.tolist()) == list(range(n_xcc))
+    assert np.array_equal(xcc, first[b % n_xcc])
+
+
 def test_priority_is_refused(c3gpu):
     with pytest.raises(c3gpu.C3Error) as e:
         c3gpu.c3_stream_create(None, priority=-1)
