@@ -367,7 +367,6 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
         constexpr bool BA = decltype(ba_c)::value;
         constexpr bool RA = decltype(ra_c)::value;
         constexpr bool NX = decltype(nx_c)::value;
-        const int s = kt & (NSTAGE - 1);
         const int s3 = (kt + NSTAGE - 1) & (NSTAGE - 1);
         const int k3 = (kt + NSTAGE - 1) * BK;
         i32x4_t rB3{};
@@ -806,7 +805,6 @@ namespace sk {
 constexpr int BM = 16, BN = 256, BK = 64, NT = 256;  // BM: one MFMA tile row block
 constexpr int B_STAGE = BK * BN * 2;                 // 32 KiB
 constexpr int B_LD = BK * BN / 8 / NT;               // 8
-constexpr int MAX_MT = 4;                            // up to 64 rows per workgroup
 }  // namespace sk
 
 // grid: x = N tiles of 256, y = K splits, z = M blocks of 16*MT rows. Each workgroup covers k in
