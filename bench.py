@@ -63,6 +63,9 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 METRIC = "concurrent GEMM TFLOP/s + copy GB/s; realized % of ideal C3 speedup"
 FLUSH_BYTES = 512 * MiB
+# Rounds of the MFMA rate probe run before every run of the C3 mode (about 2.6 ms on 256 CUs): a
+# fixed MFMA load that puts the chip in the same power state before every cell.
+PRECOND_ITERS = 8400
 
 
 def log(*a):
@@ -112,6 +115,8 @@ def parse():
                         "-2 = no hybrid cell)")
     p.add_argument("--shapes", default="",
                    help="gemm_vs_vendor: comma-separated MxNxK list instead of the workloads' shapes")
+    p.add_argument("--no-precondition", action="store_true",
+                   help="c3 mode: no fixed MFMA load before each run (the earlier protocol)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--profile", action="store_true",
@@ -384,6 +389,20 @@ def run_c3(args, c3, info):
                  for name, mv in movers}
     iso_g_opts = c3.conc_opts(gemm_mask=gmask, flush_bytes=FLUSH_BYTES)
     iso_c_opts = c3.conc_opts(flush_bytes=FLUSH_BYTES)
+    # Every run starts from the same power state. The chip's clock follows its recent load: it
+    # falls during light or memory-bound work (a lone copy, the checks) and climbs back under
+    # MFMA load, so a GEMM launched after a light run starts slower than one launched after a
+    # heavy run. Before each run, timed or not, a fixed MFMA load of about 2.6 ms brings the chip
+    # to the state a GEMM in a busy training step starts from; then come the poison and the flush,
+    # the same for every cell. Without it the concurrent step, which always follows its mover's
+    # lone copy, started from a lower clock than the isolated GEMM.
+    torch = s.torch
+    probe_out = torch.empty(info["n_cu"] * 256, dtype=torch.float64, device="cuda:0")
+
+    def precondition():
+        if not args.no_precondition:
+            c3.c3_probe_mfma_rate(probe_out, info["n_cu"], PRECOND_ITERS, 1, None)
+
     hybrid_pm = None
     if args.hybrid_permille != -2:
         hybrid_pm = args.hybrid_permille
@@ -391,10 +410,12 @@ def run_c3(args, c3, info):
             # the engines' share from isolated times (best of two untimed runs of each)
             cal = {"gemm": [], "sdma": [], "cu": []}
             for _ in range(2):
+                precondition()
                 s.poison()
                 cal["gemm"].append(c3.c3_run_concurrent(s.gargs, None, iso_g_opts)["t_conc_ns"])
                 s.verify_c("calibration GEMM")
                 for name in ("sdma", "cu"):
+                    precondition()
                     s.poison()
                     cal[name].append(c3.c3_run_concurrent(None, copy_args[name][0],
                                                           iso_c_opts)["t_conc_ns"])
@@ -418,7 +439,6 @@ def run_c3(args, c3, info):
     t_gemm, g_gpu = [], []
     rec = {name: {"t_copy": [], "c_gpu": [], "t_conc": [], "gk": [], "rs": [], "done": []}
            for name, _ in movers}
-    torch = s.torch
     torch.cuda.synchronize()
     state_before = gpu_state()
     wall0 = time.time()
@@ -436,6 +456,7 @@ def run_c3(args, c3, info):
         random.Random(1000 + i).shuffle(order)
         for name in order:
             if name == "gemm":
+                precondition()
                 s.poison()
                 t = c3.c3_run_concurrent(s.gargs, None, iso_g_opts)
                 s.verify_c(f"isolated GEMM {i}")
@@ -445,6 +466,7 @@ def run_c3(args, c3, info):
                 continue
             ca = copy_args[name][0]
             r = rec[name]
+            precondition()
             s.poison()
             t = c3.c3_run_concurrent(None, ca, iso_c_opts)
             s.verify_copy(f"isolated {name} copy {i}")
@@ -452,6 +474,7 @@ def run_c3(args, c3, info):
                 r["t_copy"].append(t["t_conc_ns"] * 1e-9)
                 r["c_gpu"].append(t["copy_gpu_ms"] * 1e-3)
                 r["rs"].append(t["reduce_gpu_ms"] * 1e-3)
+            precondition()
             s.poison()
             t = c3.c3_run_concurrent(s.gargs, ca, conc[name])
             s.verify_copy(f"{name} step {i}")
@@ -555,7 +578,9 @@ def run_c3(args, c3, info):
                   "metrics use the median of each of T_gemm, T_copy and T_conc, with the per-round "
                   "uplift quartiles beside them; copy_gbps_concurrent = the copy's bytes over the "
                   "median time from the first issue to its own completion; isolated and concurrent "
-                  "runs interleaved per step, each after a poison + 512 MiB read flush",
+                  "runs interleaved per step, each after a fixed MFMA load of about 2.6 ms (the "
+                  "same power state for every cell; off with --no-precondition), a poison and a "
+                  "512 MiB read flush",
         "wall_s_timed_rounds": round(wall, 3),
         "verified": "every run: each copy destination range equal to its source (device compare; "
                     "all-reduce: the reduced chunk equal to the fp32 rank-order sum done with "
