@@ -116,12 +116,32 @@ def parse():
     p.add_argument("--shapes", default="",
                    help="gemm_vs_vendor: comma-separated MxNxK list instead of the workloads' shapes")
     p.add_argument("--no-precondition", action="store_true",
-                   help="c3 mode: no fixed MFMA load before each run (the earlier protocol)")
+                   help="c3 and grid modes: no fixed MFMA load before each run (the earlier protocol)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--profile", action="store_true",
                    help="no verification or CPU baseline (for rocprofv3 runs)")
     return p.parse_args()
+
+
+def make_preconditioner(c3, info, args):
+    """Every run of the C3 and grid modes starts from the same power state. The chip's clock
+    follows its recent load: it falls during light or memory-bound work (a lone copy, the checks)
+    and climbs back under MFMA load, so a GEMM launched after a light run starts slower than one
+    launched after a heavy run. Before each run, timed or not, a fixed MFMA load of about 2.6 ms
+    (c3_probe_mfma_rate) brings the chip to the state a GEMM in a busy training step starts from;
+    then come the poison and the flush, the same for every cell. Without it a concurrent step that
+    always follows its mover's lone copy started from a lower clock than the isolated GEMM.
+    `--no-precondition` turns it off (the earlier protocol)."""
+    import torch
+
+    probe_out = torch.empty(info["n_cu"] * 256, dtype=torch.float64, device="cuda:0")
+
+    def precondition():
+        if not args.no_precondition:
+            c3.c3_probe_mfma_rate(probe_out, info["n_cu"], PRECOND_ITERS, 1, None)
+
+    return precondition
 
 
 class Setup:
@@ -389,20 +409,8 @@ def run_c3(args, c3, info):
                  for name, mv in movers}
     iso_g_opts = c3.conc_opts(gemm_mask=gmask, flush_bytes=FLUSH_BYTES)
     iso_c_opts = c3.conc_opts(flush_bytes=FLUSH_BYTES)
-    # Every run starts from the same power state. The chip's clock follows its recent load: it
-    # falls during light or memory-bound work (a lone copy, the checks) and climbs back under
-    # MFMA load, so a GEMM launched after a light run starts slower than one launched after a
-    # heavy run. Before each run, timed or not, a fixed MFMA load of about 2.6 ms brings the chip
-    # to the state a GEMM in a busy training step starts from; then come the poison and the flush,
-    # the same for every cell. Without it the concurrent step, which always follows its mover's
-    # lone copy, started from a lower clock than the isolated GEMM.
     torch = s.torch
-    probe_out = torch.empty(info["n_cu"] * 256, dtype=torch.float64, device="cuda:0")
-
-    def precondition():
-        if not args.no_precondition:
-            c3.c3_probe_mfma_rate(probe_out, info["n_cu"], PRECOND_ITERS, 1, None)
-
+    precondition = make_preconditioner(c3, info, args)
     hybrid_pm = None
     if args.hybrid_permille != -2:
         hybrid_pm = args.hybrid_permille
@@ -654,6 +662,7 @@ def run_grid(args, c3, info):
     per = info["n_cu"] // info["n_xcc"]
     keeps = (per, per * 7 // 8, per * 3 // 4)
     reps = max(3, args.steps)
+    precondition = make_preconditioner(c3, info, args)
     for total in base.sweep_total_bytes:
         w = base.with_gather_total(total)
         s = Setup(c3, w, check=not args.profile)
@@ -663,6 +672,7 @@ def run_grid(args, c3, info):
         pm = args.hybrid_permille
         for i in range(reps + 1):
             rnd = {}
+            precondition()
             s.poison()
             rnd["gemm"] = c3.c3_run_concurrent(s.gargs, None, c3.conc_opts(flush_bytes=FLUSH_BYTES))["t_conc_ns"]
             s.verify_c("grid isolated GEMM")
@@ -681,6 +691,7 @@ def run_grid(args, c3, info):
                 else:
                     mv = c3.C3_MOVER_CU if mname == "cu" else c3.C3_MOVER_SDMA
                     ca, _keep = s.cargs(mv)
+                precondition()
                 s.poison()
                 rnd[("copy", mname)] = c3.c3_run_concurrent(None, ca, c3.conc_opts(flush_bytes=FLUSH_BYTES))["t_conc_ns"]
                 s.verify_copy("grid isolated copy")
@@ -688,6 +699,7 @@ def run_grid(args, c3, info):
                     gm = None if keep == per else c3.c3_cu_mask_balanced(keep)
                     cm = None if (keep == per or mv == c3.C3_MOVER_SDMA) else c3.c3_cu_mask_balanced(keep, True)
                     for cf in (False, True):
+                        precondition()
                         s.poison()
                         t = c3.c3_run_concurrent(s.gargs, ca, c3.conc_opts(
                             gemm_mask=gm, comm_mask=cm, comm_first=cf, flush_bytes=FLUSH_BYTES))
