@@ -42,6 +42,10 @@ def test_defaults(monkeypatch):
     a = b.parse()
     assert (a.gpus, a.steps, a.warmup, a.mode, a.workload) == (1, 20, 3, "c3", 4)
     assert b.PEAK_BF16_TFLOPS == 2500.0 and b.PEAK_HBM_GBPS == 8000.0
+    # every run of the C3 and grid modes starts after the fixed MFMA load unless asked otherwise
+    assert a.no_precondition is False and b.PRECOND_ITERS > 0
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--no-precondition"])
+    assert b.parse().no_precondition is True
 
 
 def test_traffic_record_lookup_is_consistent():
