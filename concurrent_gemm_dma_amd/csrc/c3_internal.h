@@ -137,8 +137,11 @@ c3_status sdma_discover();
 void sdma_release();
 
 struct SdmaOp {
-    std::vector<hsa_signal_t> signals;  // one per chunk
-    std::vector<uint32_t> engine_of;    // engine id per chunk
+    std::vector<Segment> chunks;        // the transfers, in issue order
+    std::vector<uint32_t> engines;      // engine ids; chunk i goes to engines[i mod n]
+    size_t next = 0;                    // first chunk not yet taken up (issued or faked)
+    std::vector<hsa_signal_t> signals;  // one per chunk taken up
+    std::vector<uint32_t> engine_of;    // engine id per chunk taken up
     std::vector<int> issued;            // 1 if the chunk was handed to ROCr
     uint32_t engines_used = 0;
     int fault_mode = 0;
@@ -146,7 +149,14 @@ struct SdmaOp {
     int64_t deadline_ns = 0;
 };
 // Split segments into chunks and issue them on the engines (host returns right after issue).
-c3_status sdma_issue(const std::vector<Segment>& segs, const c3_move_opts& o, SdmaOp* op);
+// With first_round_only, only the first chunk of each engine is issued; sdma_issue_rest issues
+// the others. An engine runs its transfers in issue order, so the rest only queue behind the
+// first round. On an error nothing is left in flight and the op counts as never issued.
+c3_status sdma_issue(const std::vector<Segment>& segs, const c3_move_opts& o, SdmaOp* op,
+                     bool first_round_only = false);
+// Issue the chunks sdma_issue held back. On an error the op still needs sdma_finish, which
+// waits for everything issued.
+c3_status sdma_issue_rest(SdmaOp* op);
 // Nonblocking: true once every chunk's signal has left the "pending" state.
 bool sdma_done(const SdmaOp& op);
 // Wait for all chunks (bounded by the op's deadline), collect errors and timestamps, and return

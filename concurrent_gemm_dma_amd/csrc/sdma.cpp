@@ -159,7 +159,53 @@ void sdma_release() {
     profiling_on = false;
 }
 
-c3_status sdma_issue(const std::vector<Segment>& segs, const c3_move_opts& o, SdmaOp* op) {
+namespace {
+
+// Hand chunks op->next .. end-1 to ROCr, chunk i on engine engines[i mod n]. On an error the
+// chunk that failed is marked complete and not issued; what was issued before it stays in the
+// op for sdma_finish to drain.
+c3_status issue_chunks(SdmaOp* op, size_t end) {
+    Context& c = ctx();
+    for (size_t& i = op->next; i < end; ++i) {
+        hsa_signal_t sig;
+        C3_TRY(get_signal(&sig));
+        const uint32_t engine = op->engines[i % op->engines.size()];
+        const Segment& ch = op->chunks[i];
+        op->signals.push_back(sig);
+        op->engine_of.push_back(engine);
+        const bool faulted = op->fault_mode != C3_FAULT_NONE && (int)i == op->fault_chunk;
+        if (faulted) {
+            const hsa_signal_value_t v = op->fault_mode == C3_FAULT_DROP_CHUNK  ? 0
+                                         : op->fault_mode == C3_FAULT_ERROR_CHUNK ? -1
+                                                                                  : 1;
+            hsa_signal_store_screlease(sig, v);
+            op->issued.push_back(0);
+            continue;
+        }
+        hsa_signal_store_screlease(sig, 1);
+        const hsa_status_t hs = hsa_amd_memory_async_copy_on_engine(
+            ch.dst, c.agent, ch.src, c.agent, ch.bytes, 0, nullptr, sig,
+            (hsa_amd_sdma_engine_id_t)engine, true);
+        if (hs != HSA_STATUS_SUCCESS) {
+            // nothing was queued for this chunk: mark it complete
+            hsa_signal_store_screlease(sig, 0);
+            op->issued.push_back(0);
+            const char* m = nullptr;
+            hsa_status_string(hs, &m);
+            const size_t failed = i++;
+            return fail(C3_E_HSA, "hsa_amd_memory_async_copy_on_engine(chunk %zu, engine 0x%x, %llu B): %s",
+                        failed, engine, (unsigned long long)ch.bytes, m ? m : "?");
+        }
+        op->issued.push_back(1);
+        op->engines_used |= engine;
+    }
+    return C3_OK;
+}
+
+}  // namespace
+
+c3_status sdma_issue(const std::vector<Segment>& segs, const c3_move_opts& o, SdmaOp* op,
+                     bool first_round_only) {
     Context& c = ctx();
     std::vector<uint32_t> engines;
     for (uint32_t e : c.sdma_engines)
@@ -169,11 +215,6 @@ c3_status sdma_issue(const std::vector<Segment>& segs, const c3_move_opts& o, Sd
                     "no SDMA engine for device-local copies (available mask 0x%x, requested 0x%x)",
                     c.info.sdma_engine_mask, o.engine_mask);
 
-    struct Chunk {
-        const char* src;
-        char* dst;
-        uint64_t bytes;
-    };
     // Default split: one transfer per segment (shard or block), each cut into just enough
     // pieces that there are at least as many transfers as engines (one engine moves only
     // ~100 GB/s, so a gather of 8 shards would otherwise leave half of 16 engines idle).
@@ -188,7 +229,9 @@ c3_status sdma_issue(const std::vector<Segment>& segs, const c3_move_opts& o, Sd
     for (const Segment& s : segs) nonempty += s.bytes != 0;
     const uint64_t pieces =
         nonempty ? std::max<uint64_t>(1, (engines.size() + nonempty - 1) / nonempty) : 1;
-    std::vector<Chunk> chunks;
+    const int timeout_ms = o.timeout_ms > 0 ? o.timeout_ms : 20000;
+
+    *op = SdmaOp{};
     for (const Segment& s : segs) {
         if (s.bytes == 0) continue;
         uint64_t step = o.chunk_bytes;
@@ -199,56 +242,25 @@ c3_status sdma_issue(const std::vector<Segment>& segs, const c3_move_opts& o, Sd
             step = (step + 255) & ~uint64_t(255);  // 256-byte multiples keep pieces aligned
         }
         for (uint64_t off = 0; off < s.bytes; off += step)
-            chunks.push_back({static_cast<const char*>(s.src) + off, static_cast<char*>(s.dst) + off,
-                              std::min(step, s.bytes - off)});
+            op->chunks.push_back({static_cast<const char*>(s.src) + off,
+                                  static_cast<char*>(s.dst) + off, std::min(step, s.bytes - off)});
     }
-    const int timeout_ms = o.timeout_ms > 0 ? o.timeout_ms : 20000;
-
-    *op = SdmaOp{};
+    op->engines = std::move(engines);
     op->fault_mode = o.fault_mode;
     op->fault_chunk = o.fault_chunk;
     op->deadline_ns = now_ns() + (int64_t)timeout_ms * 1000000ll;
-    op->signals.reserve(chunks.size());
-    for (size_t i = 0; i < chunks.size(); ++i) {
-        hsa_signal_t sig;
-        c3_status st = get_signal(&sig);
-        if (st != C3_OK) {
-            c3_timing ignore{};
-            (void)sdma_finish(op, &ignore);
-            return st;
-        }
-        const uint32_t engine = engines[i % engines.size()];
-        op->signals.push_back(sig);
-        op->engine_of.push_back(engine);
-        const bool faulted = o.fault_mode != C3_FAULT_NONE && (int)i == o.fault_chunk;
-        if (faulted) {
-            const hsa_signal_value_t v = o.fault_mode == C3_FAULT_DROP_CHUNK  ? 0
-                                         : o.fault_mode == C3_FAULT_ERROR_CHUNK ? -1
-                                                                                : 1;
-            hsa_signal_store_screlease(sig, v);
-            op->issued.push_back(0);
-            continue;
-        }
-        hsa_signal_store_screlease(sig, 1);
-        const hsa_status_t hs = hsa_amd_memory_async_copy_on_engine(
-            chunks[i].dst, c.agent, chunks[i].src, c.agent, chunks[i].bytes, 0, nullptr, sig,
-            (hsa_amd_sdma_engine_id_t)engine, true);
-        if (hs != HSA_STATUS_SUCCESS) {
-            // nothing was queued for this chunk: mark it complete and drain the others
-            hsa_signal_store_screlease(sig, 0);
-            op->issued.push_back(0);
-            const char* m = nullptr;
-            hsa_status_string(hs, &m);
-            c3_timing ignore{};
-            (void)sdma_finish(op, &ignore);
-            return fail(C3_E_HSA, "hsa_amd_memory_async_copy_on_engine(chunk %zu, engine 0x%x, %llu B): %s",
-                        i, engine, (unsigned long long)chunks[i].bytes, m ? m : "?");
-        }
-        op->issued.push_back(1);
-        op->engines_used |= engine;
+    op->signals.reserve(op->chunks.size());
+    const size_t n = op->chunks.size();
+    const c3_status st = issue_chunks(op, first_round_only ? std::min(n, op->engines.size()) : n);
+    if (st != C3_OK) {
+        // drain what was issued; the caller treats the op as never issued
+        c3_timing ignore{};
+        (void)sdma_finish(op, &ignore);
     }
-    return C3_OK;
+    return st;
 }
+
+c3_status sdma_issue_rest(SdmaOp* op) { return issue_chunks(op, op->chunks.size()); }
 
 bool sdma_done(const SdmaOp& op) {
     for (hsa_signal_t s : op.signals)

@@ -152,7 +152,9 @@ typedef struct {
     uint32_t gemm_cu_mask[C3_MAX_MASK_WORDS]; /* all zero = every CU */
     uint32_t comm_cu_mask[C3_MAX_MASK_WORDS]; /* all zero = every CU (CU-mover copies and any
                                                  reduce-scatter) */
-    int32_t comm_first;   /* 1 = issue the communication before the GEMM */
+    int32_t comm_first;   /* 1 = start the communication before the GEMM (SDMA: each engine's
+                             first transfer is issued before the GEMM launch, the engine's
+                             other transfers right after it, queued behind the first) */
     int32_t use_priority; /* must be 0: every stream stays at default priority; the
                              prioritization control is the issue order (comm_first) */
     uint64_t flush_bytes; /* > 0: before the timed region, read this many bytes of a library

@@ -252,6 +252,51 @@ def test_concurrent_all2all(c3gpu):
                             ("sdma", 28, False)])
 
 
+def test_comm_first_issues_later_transfers_after_the_gemm(c3gpu):
+    """Communication first beside a GEMM with more transfers than engines (an 8 x 8 all-to-all of
+    256 KiB blocks, one transfer per block): each engine's first transfer goes before the GEMM
+    launch and the others right after it. All 64 are issued and land byte-exact; a dropped,
+    failed or stuck transfer among the later ones is caught or reported like one among the
+    first, after both operations finished, with C unchanged; the library stays usable."""
+    n_eng = bin(c3gpu.c3_device_info()["sdma_engine_mask"]).count("1")
+    ub = 256 * KiB
+    case = Case(c3gpu, 1024, 1032, 1024, "all2all", 8, ub, 9150)
+    case.poison(0)
+    c3gpu.c3_run_concurrent(case.gargs(c3gpu), None)
+    iso_c = bf16_from_dev(case.dC)
+    first = c3gpu.conc_opts(comm_first=True)
+
+    def run(rep, **fault):
+        case.poison(rep)
+        cargs, _keep = case.cargs(c3gpu, c3gpu.C3_MOVER_SDMA,
+                                  c3gpu.move_opts(chunk_bytes=ub, **fault))
+        try:
+            return c3gpu.c3_run_concurrent(case.gargs(c3gpu), cargs, first)
+        finally:
+            np.testing.assert_array_equal(bf16_from_dev(case.dC), iso_c, err_msg=str(fault))
+
+    t = run(1)
+    case.check_comm("comm-first, 64 transfers")
+    assert t["n_chunks"] == 64 and t["comm_issued_first"] == 1
+    late = min(n_eng + 3, 63)  # issued after the GEMM launch
+    print(f"engines {n_eng}, faulted transfer {late}", flush=True)
+    # dropped: the call succeeds and exactly that transfer's block is stale
+    run(2, fault_mode=c3gpu.C3_FAULT_DROP_CHUNK, fault_chunk=late)
+    got = bytes_from_dev(case.dst)
+    d = (late % 8) * 8 + late // 8  # source block (late // 8, late % 8) lands at block d
+    assert oracle.first_diff(case.want[d * ub:(d + 1) * ub], got[d * ub:(d + 1) * ub]) != -1
+    assert oracle.first_diff(case.want[:d * ub], got[:d * ub]) == -1
+    assert oracle.first_diff(case.want[(d + 1) * ub:], got[(d + 1) * ub:]) == -1
+    with pytest.raises(c3gpu.C3Error) as e:
+        run(3, fault_mode=c3gpu.C3_FAULT_ERROR_CHUNK, fault_chunk=late)
+    assert e.value.status == c3gpu.C3_E_HSA
+    with pytest.raises(c3gpu.C3Error) as e:
+        run(4, fault_mode=c3gpu.C3_FAULT_STUCK_CHUNK, fault_chunk=63, timeout_ms=300)
+    assert e.value.status == c3gpu.C3_E_TIMEOUT
+    run(5)
+    case.check_comm("comm-first after the faults")
+
+
 def test_concurrent_skinny_gemm(c3gpu):
     case = Case(c3gpu, 16, 4096, 2048, "gather", 8, 2 * MiB + 16, 9200)
     run_cells(c3gpu, case, [("cu", 32, True), ("sdma", 32, True), ("sdma", 28, False)])
