@@ -346,8 +346,10 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_tile256_dma(
             else rlo[set][ni] = v;
         }
     };
+    // The 16 MFMAs of a k-slice walk the 4x4 blocks row by row, odd rows backwards, so that from
+    // one MFMA to the next only one operand changes (the row operand at a row's end stays).
     auto mfma_item = [&](int set, int i) {
-        const int mi = i >> 2, ni = i & 3;
+        const int mi = i >> 2, ni = (mi & 1) ? 3 - (i & 3) : (i & 3);
         const i16x8_t rv = __builtin_shufflevector(rlo[set][ni], rhi[set][ni], 0, 1, 2, 3, 4, 5, 6, 7);
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, rv),
                                                               cf[set][mi], acc[mi][ni], 0, 0, 0);
