@@ -49,22 +49,26 @@ def test_defaults(monkeypatch):
 
 
 def test_traffic_record_lookup_is_consistent():
+    """Every record in the traffic file names a kernel and a workload the benchmark knows; while
+    its source hash matches, the lookup returns the calibrated bytes, at least the workload's
+    algorithmic GEMM bytes."""
     b = load_bench()
     from concurrent_gemm_dma_amd import workloads as wl
 
-    w = wl.WORKLOADS[2]
+    by_name = {w.name: w for w in wl.WORKLOADS.values()}
     rec = json.load(open(os.path.join(ROOT, "profiles", "gemm_traffic.json")))
-    key = f"gemm_bf16_tile256_dma@{w.name}"
-    t = b.measured_traffic("gemm_bf16_tile256_dma", w)
-    if rec[key]["source_sha256"] == b.kernel_source_hash():
-        r = rec[key]
-        want = int(r["fetch_kib"] * 1024 * r["fetch_scale"] + r["write_kib"] * 1024 * r["write_scale"])
-        assert t == want
-        # the GEMM moves at least its algorithmic bytes
-        assert t >= w.gemm_bytes
-    else:
-        assert t is None
-    assert b.measured_traffic("no_such_kernel", w) is None
+    assert "gemm_bf16_tile256_dma@" + wl.WORKLOADS[2].name in rec
+    for key, r in rec.items():
+        kernel, name = key.rsplit("@", 1)
+        w = by_name[name]
+        t = b.measured_traffic(kernel, w)
+        if r["source_sha256"] == b.kernel_source_hash():
+            want = int(r["fetch_kib"] * 1024 * r["fetch_scale"] + r["write_kib"] * 1024 * r["write_scale"])
+            assert t == want, key
+            assert t >= w.gemm_bytes, key
+        else:
+            assert t is None, key
+        assert b.measured_traffic("no_such_kernel", w) is None
 
 
 def test_gpu_state_never_raises():
