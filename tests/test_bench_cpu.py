@@ -40,7 +40,7 @@ def test_defaults(monkeypatch):
     b = load_bench()
     monkeypatch.setattr(sys, "argv", ["bench.py"])
     a = b.parse()
-    assert (a.gpus, a.steps, a.warmup, a.mode, a.workload) == (1, 20, 3, "c3", 4)
+    assert (a.gpus, a.steps, a.warmup, a.mode, a.workload) == (1, 50, 3, "c3", 4)
     assert b.PEAK_BF16_TFLOPS == 2500.0 and b.PEAK_HBM_GBPS == 8000.0
     # every run of the C3 and grid modes starts after the fixed MFMA load unless asked otherwise
     assert a.no_precondition is False and b.PRECOND_ITERS > 0
@@ -104,6 +104,7 @@ def test_mover_cell_aggregates_by_the_documented_rules():
     assert res["gemm_slowdown"] == pytest.approx(om.gemm_slowdown(Tg, Tx), rel=1e-12)
     per = sorted(om.uplift_fraction(a, c, x) for a, c, x in zip(t_gemm, r["t_copy"], r["t_conc"]))
     assert res["uplift_per_round_p25_median_p75"] == pytest.approx([per[1], per[2], per[3]])
+    assert res["uplift_paired_median"] == pytest.approx(per[2])
     assert res["copy_gbps_concurrent"] == pytest.approx(comm_bytes / 0.80e-3 / 1e9)
     assert res["gemm_tflops_concurrent"] == pytest.approx(flops / statistics.mean(r["t_conc"]) / 1e12)
     assert res["speedup_vs_best_serial"] == pytest.approx((Tg + 0.5e-3) / Tx)
