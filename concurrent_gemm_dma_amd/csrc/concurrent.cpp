@@ -8,8 +8,9 @@
 //   CU-mover copy runs on a second masked stream (typically the complement). Every library
 //   stream carries an explicit mask (all CUs when unrestricted) so that each gets a hardware
 //   queue of its own and the two operations can really overlap.
-// * Prioritization: the communication is issued before the GEMM (comm_first). Streams keep the
-//   default priority.
+// * Prioritization: the communication is issued before the GEMM (comm_first); with the SDMA
+//   engines, each engine's first transfer goes before the GEMM launch and its others right after
+//   it, queued behind the first. Streams keep the default priority.
 // * Completion: the host polls the GEMM's end event and the copy's end event (CU mover) or
 //   completion signals (SDMA mover) and timestamps each completion on a monotonic clock.
 // * All-reduce (reduce-scatter + all-gather; L3 Synthesis page on 2412.14335, section 3,
