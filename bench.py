@@ -38,6 +38,8 @@ Other modes print one JSON line per measured cell:
                    cost against per-K-step cost)
   --mode mfma_ceiling  the matrix cores' sustained bf16 rate with nothing but MFMAs in flight
                    (the power-limited ceiling for any GEMM kernel on this chip)
+  --mode gemm_data the tile GEMM of workloads 2 and 4 on the workloads' operand distributions,
+                   small integers and zeros (same cycles, clock set by the operands' power)
   --mode gemm_vs_vendor  the library's GEMM against torch.matmul (hipBLASLt) on the same
                    operands, alternating single launches and back-to-back batches (a reference
                    point for kernel quality; torch's result is not used for anything else)
@@ -101,7 +103,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--mode", default="c3",
                    choices=["c3", "movers", "grid", "cus", "partition", "gemm_vs_vendor",
-                            "hybrid", "ksteps", "mfma_ceiling"])
+                            "hybrid", "ksteps", "mfma_ceiling", "gemm_data"])
     p.add_argument("--workload", type=int, default=4,
                    help="workload id (1..6); 4 = the 405B-class GEMM beside the 512 MiB all-to-all")
     p.add_argument("--gather-mib", type=int, default=0, help="workload 5: total gather MiB")
@@ -1044,6 +1046,65 @@ def run_mfma_ceiling(args, c3, info):
                           "ms_min": round(min(ms), 4), "ms_max": round(max(ms), 4)}), flush=True)
 
 
+def run_gemm_data(args, c3, info):
+    """The tile GEMM of workloads 2 and 4 on three kinds of operands: the workloads' distributions
+    (bf16 of N(0, 1) activations and N(0, 0.02) weights), small integers in -2..2 and zeros. The kernel
+    runs the same instructions on all three, so its cycles are the same; what changes is how
+    many operand bits switch in the matrix cores, and with it the power the chip spends per FLOP
+    and so the clock its power limit allows. Every launch comes after the fixed MFMA load and a
+    512 MiB read flush (as in the c3 mode); kinds in an order shuffled per round; HIP-event time
+    of the GEMM's launch (medians). C is checked bit-identical across rounds (and zero for zero
+    operands)."""
+    import torch
+
+    from concurrent_gemm_dma_amd import workloads as wl
+
+    precondition = make_preconditioner(c3, info, args)
+    o = c3.conc_opts(flush_bytes=FLUSH_BYTES)
+    reps = max(3, args.steps)
+    for w in (wl.WORKLOADS[2], wl.WORKLOADS[4]):
+        M, N, K = w.M, w.N, w.K
+        g = torch.Generator(device="cuda").manual_seed(w.wid)
+        A = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        B = (torch.randn(K, N, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        ops = {"workload data": (A, B),
+               "small integers": (torch.randint(-2, 3, (M, K), device="cuda", generator=g).to(torch.bfloat16),
+                                  torch.randint(-2, 3, (K, N), device="cuda", generator=g).to(torch.bfloat16)),
+               "zeros": (torch.zeros_like(A), torch.zeros_like(B))}
+        C = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+        kinds = list(ops)
+        times = {k: [] for k in kinds}
+        first = {}
+        for i in range(reps + 1):
+            order = list(kinds)
+            random.Random(i).shuffle(order)
+            for k in order:
+                a, b = ops[k]
+                C.fill_(-1)
+                torch.cuda.synchronize()
+                precondition()
+                t = c3.c3_run_concurrent(c3.gemm_args(a, b, C, M, N, K), None, o)
+                if not args.profile:
+                    if k not in first:
+                        first[k] = C.clone()
+                        if k == "zeros" and bool(C.any()):
+                            raise SystemExit("gemm_data: C of zero operands is not zero")
+                    elif not torch.equal(first[k], C):
+                        raise SystemExit(f"gemm_data: C of {k} differs between rounds")
+                if i:
+                    times[k].append(t["gemm_gpu_ms"])
+        flops = 2.0 * M * N * K
+        for k in kinds:
+            ms = statistics.median(times[k])
+            print(json.dumps({"mode": "gemm_data", "workload": w.name, "M": M, "N": N, "K": K,
+                              "operands": k, "gemm_ms": round(ms, 4),
+                              "tflops": round(flops / ms / 1e9, 1),
+                              "frac_of_peak": round(flops / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}),
+                  flush=True)
+        del ops, A, B, C, first
+        torch.cuda.empty_cache()
+
+
 def run_gemm_vs_vendor(args, c3, info):
     """The library's GEMM and torch.matmul (hipBLASLt) on the same bf16 operands: alternating
     event-timed single launches (median), then two batches of 20 back-to-back launches each.
@@ -1188,7 +1249,8 @@ def main():
     log("device:", info)
     {"c3": run_c3, "movers": run_movers, "grid": run_grid, "cus": run_cus, "hybrid": run_hybrid,
      "partition": run_partition, "gemm_vs_vendor": run_gemm_vs_vendor,
-     "ksteps": run_ksteps, "mfma_ceiling": run_mfma_ceiling}[args.mode](args, c3, info)
+     "ksteps": run_ksteps, "mfma_ceiling": run_mfma_ceiling,
+     "gemm_data": run_gemm_data}[args.mode](args, c3, info)
     c3.c3_finalize()
 
 
