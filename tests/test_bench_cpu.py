@@ -46,6 +46,12 @@ def test_defaults(monkeypatch):
     assert a.no_precondition is False and b.PRECOND_ITERS > 0
     monkeypatch.setattr(sys, "argv", ["bench.py", "--no-precondition"])
     assert b.parse().no_precondition is True
+    # 50 timed rounds only in the c3 mode; the sweeps keep 20; an explicit count always wins
+    for mode in ("grid", "partition", "gemm_data", "mfma_ceiling"):
+        monkeypatch.setattr(sys, "argv", ["bench.py", "--mode", mode])
+        assert b.parse().steps == 20, mode
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--steps", "7"])
+    assert b.parse().steps == 7
 
 
 def test_traffic_record_lookup_is_consistent():
